@@ -1,0 +1,50 @@
+"""Plain, slow, fp64 CPU oracle for the streaming pyramid denoiser's hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, constants or
+helpers with the HIP path in ``streaming_diffusion_portrait_amd``.
+
+Sources (cited by page and section; the pages are the PersonaLive write-up on
+juhe.plus, "PersonaLive" for short, and the hysenlabs repository review):
+
+* ``attention``  -- reference-bank spatial self-attention
+  (PersonaLive, section "三条条件通路" / three conditioning paths: the 16
+  reference-layer features are concatenated with the denoiser's own K/V for
+  spatial self-attention).
+* ``ddim``       -- the per-window DDIM step of the streaming pyramid
+  (PersonaLive, sections "它解决什么" / specification and
+  "流式金字塔去噪" / streaming pyramid denoising).
+* ``motion``     -- the motion-bank minimum-L2 drift check
+  (PersonaLive, section "抗身份漂移的补丁" / anti identity-drift patch).
+* ``pile``       -- the ``latents_pile`` queue state machine
+  (PersonaLive, section "流式金字塔去噪").
+
+Every floating-point computation here is float64.  Each function states the
+passage it follows; readings of points the pages leave open are listed in the
+repository's design notes.  Parity status: every function here is pinned by
+``tests/test_oracle_*.py`` against brute force, closed forms, invariants or a
+library routine; none is "parity unpinned".
+"""
+
+from .attention import refbank_attention, attend_rows, concat_segments
+from .ddim import (
+    sd_scaled_linear_alphas_cumprod,
+    ddim_coefficients,
+    ddim_step,
+    pyramid_ddim_step,
+)
+from .motion import motion_bank_min_l2
+from .pile import PyramidPile
+
+__all__ = [
+    "refbank_attention",
+    "attend_rows",
+    "concat_segments",
+    "sd_scaled_linear_alphas_cumprod",
+    "ddim_coefficients",
+    "ddim_step",
+    "pyramid_ddim_step",
+    "motion_bank_min_l2",
+    "PyramidPile",
+]
