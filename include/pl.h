@@ -1,0 +1,219 @@
+/*
+ * pl.h -- C ABI of the MI355X (gfx950) hot path of the PersonaLive streaming
+ * pyramid denoiser: reference-bank spatial self-attention, the per-window
+ * DDIM step of the latents pile, the motion-bank drift check, and the pile's
+ * integer state machine.
+ *
+ * Sources are cited by page and section: "PersonaLive" is the PersonaLive
+ * write-up on juhe.plus (sections 它解决什么 / specification, 流式金字塔去噪 /
+ * streaming pyramid denoising, 首帧怎么办 / first frames, 抗身份漂移的补丁 /
+ * anti identity-drift patch, 三条条件通路 / three conditioning paths,
+ * TensorRT 融合 / TensorRT fusion).
+ *
+ * Conventions shared by every call
+ *   - Device pointers are HIP device addresses on the current device; host
+ *     pointers are ordinary process memory read before the call returns.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronises device memory.
+ *   - `stream` is a hipStream_t passed as `void*` (NULL = the default stream).
+ *     Work is enqueued on it and the call returns without waiting.
+ *   - Every argument is validated before anything is launched: a call that
+ *     returns an error has written nothing.  Errors are status codes; the
+ *     calling thread's pl_last_error() holds a one-line explanation.  No C++
+ *     exception crosses the ABI.  All calls are reentrant.
+ */
+#ifndef PL_H_
+#define PL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pl_status;
+#define PL_OK 0            /* success */
+#define PL_EINVAL 1        /* invalid argument (null pointer, size or index out of range) */
+#define PL_EUNSUPPORTED 2  /* valid in principle but not implemented (head dim, alignment) */
+#define PL_EDEVICE 3       /* the HIP runtime reported an error at launch */
+
+#define PL_ABI_VERSION 1
+#define PL_MAX_SEGMENTS 8       /* key segments per attention call: self + reference + anchors (5 used) */
+#define PL_MAX_WINDOWS 8        /* windows per pile (the pages use 4) */
+#define PL_MAX_MOTION_BANK 4    /* reference embedding + at most 3 anchors */
+
+/* ABI version of the loaded library (PL_ABI_VERSION at build time). */
+int32_t pl_abi_version(void);
+
+/* Static name of a status code ("PL_OK", ...); "PL_UNKNOWN" otherwise. */
+const char* pl_status_string(pl_status s);
+
+/* Thread-local text describing the calling thread's most recent failure, or
+ * "" if its last call succeeded.  Valid until that thread's next pl_* call. */
+const char* pl_last_error(void);
+
+/* ------------------------------------------------------------------------ *
+ * Reference-bank spatial self-attention (one transformer layer)
+ *
+ * PersonaLive, section 三条条件通路: the Reference UNet writes each layer's
+ * features into a bank once per stream; the denoiser concatenates the layer's
+ * bank features with its own keys/values and runs spatial self-attention.
+ * Section 抗身份漂移的补丁: each drift anchor appends one more entry per
+ * layer; section TensorRT 融合 bounds the bank at 4x the reference length.
+ *
+ * For every frame f < F and head h < H, with rows r < Lq:
+ *   O[f, r, h*d:(h+1)*d] = softmax_j( scale * Q[f, r, h] . K_cat[f, j, h] ) V_cat[f, j, h]
+ * where the key axis j runs over the segments in order (the result does not
+ * depend on that order).  No mask, bias or dropout.
+ *
+ * Data: fp16 (IEEE binary16) everywhere; products are accumulated in fp32,
+ * the softmax is evaluated in fp32 and O is rounded to nearest even.
+ * Layout: token-major.  Row r of frame f of a tensor X starts at
+ *   X + f * frame_stride + r * ld      (elements, not bytes)
+ * and head h occupies that row's elements [h*d, (h+1)*d).  This is the
+ * layout the q/k/v projections produce, so no transposes are needed.
+ * ------------------------------------------------------------------------ */
+
+/* One source of keys/values.  The segments of a call are a virtual
+ * concatenation: nothing is copied. */
+typedef struct pl_kv_segment {
+  const void* k;         /* device fp16; row r of frame f at k + f*frame_stride + r*ld */
+  const void* v;         /* device fp16; same indexing as k */
+  int64_t len;           /* keys in this segment (>= 1) */
+  int64_t ld;            /* row stride in elements (>= H*d, multiple of 8) */
+  int64_t frame_stride;  /* elements between frames; 0 = shared by all frames (bank entries) */
+} pl_kv_segment;
+
+/* Bytes of device workspace pl_refbank_attn needs for these sizes.
+ * The current kernels need none and return 0; callers should still query it. */
+size_t pl_refbank_attn_workspace_size(int32_t F, int32_t Lq, int32_t H, int32_t d,
+                                      const int64_t* seg_len, int32_t nseg);
+
+/* Launch one reference-bank attention layer.
+ *   q, o          device fp16 [F][Lq][ld]; o must not overlap q or any K/V.
+ *   q_ld, o_ld    row strides in elements (>= H*d, multiple of 8).
+ *   *_frame_stride  elements between frames (>= Lq*ld is not required, but
+ *                 rows of different frames must not overlap in o).
+ *   F, Lq, H      frames (>= 1), query rows per frame (>= 1), heads (>= 1).
+ *   d             head dimension: 32, 40, 80 or 160 (else PL_EUNSUPPORTED).
+ *   segs, nseg    host array of 1..PL_MAX_SEGMENTS segments, total keys <= 2^24.
+ *   scale         logit scale, > 0 (usually 1/sqrt(d)).
+ *   workspace     device memory of workspace_bytes >= the size above (may be
+ *                 NULL when that size is 0).
+ * All device pointers must be 16-byte aligned (PL_EUNSUPPORTED otherwise). */
+pl_status pl_refbank_attn(const void* q, int64_t q_ld, int64_t q_frame_stride,
+                          void* o, int64_t o_ld, int64_t o_frame_stride,
+                          int32_t F, int32_t Lq, int32_t H, int32_t d,
+                          const pl_kv_segment* segs, int32_t nseg, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Per-window DDIM step of the latents pile
+ *
+ * PersonaLive, section 它解决什么: DDIM, epsilon prediction, 4 steps.
+ * Section 流式金字塔去噪: the pile holds W windows at their own timesteps
+ * (999 / 666 / 333 / 0 with a step length of 333); one forward gives every
+ * window its epsilon estimate and each window steps from t to t - step_len;
+ * the window leaving the queue hands pred_original_sample (the x0 estimate)
+ * to the VAE instead of its last sample.
+ *
+ * For window w with a = alpha_bar[t_w] and a' = alpha_bar[t_w - step_len]
+ * (a' = final_alpha_cumprod when t_w - step_len < 0), eta = 0, no clipping:
+ *   x0     = (x_t - sqrt(1 - a) * eps) / sqrt(a)
+ *   x_prev = sqrt(a') * x0 + sqrt(1 - a') * eps
+ * The host folds these into per-window coefficients in fp64; the kernel
+ * applies them in fp32 in one pass over x_t and eps.
+ *
+ *   x_t, eps      device fp32 [W][elems_per_window], window-major.
+ *   x_prev        device fp32, same shape; may alias x_t (in-place update).
+ *   x0_out        device fp32 [elems_per_window]: x0 of window emit_window.
+ *                 Required when emit_window >= 0, ignored when it is -1.
+ *   W             1..PL_MAX_WINDOWS; elems_per_window >= 1.
+ *   t_host        host int32 [W], each in [0, T).
+ *   step_len      >= 1 (333 on the pages).
+ *   alphas_cumprod_host  host fp64 [T] with values in (0, 1], or NULL for
+ *                 Stable Diffusion's scaled_linear schedule (betas from
+ *                 0.00085 to 0.012 in sqrt space, T must be 1000).
+ *   final_alpha_cumprod  a' used when t - step_len < 0; pass a negative
+ *                 value to use alpha_bar[0]; otherwise must lie in (0, 1].
+ *   emit_window   -1 or the index of the window whose x0 is written.
+ * No alignment requirement (16-byte aligned buffers take the vector path). */
+pl_status pl_pyramid_ddim_step(const float* x_t, const float* eps, float* x_prev, float* x0_out,
+                               int32_t W, int64_t elems_per_window,
+                               const int32_t* t_host, int32_t step_len,
+                               const double* alphas_cumprod_host, int32_t T,
+                               double final_alpha_cumprod, int32_t emit_window, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Motion-bank minimum-L2 drift check
+ *
+ * PersonaLive, section 抗身份漂移的补丁: the current frame's expression
+ * embedding is compared with the motion bank; if its smallest L2 distance
+ * exceeds the threshold (17 on the pages) the caller appends an anchor, at
+ * most three times per stream.  Section 三条条件通路: the embedding is the
+ * 512-dimensional MotEncoder output.
+ *
+ * For each query i: min_dist[i] = min_j ||query[i] - bank[j]||_2 (Euclidean,
+ * fp32, fixed reduction order), argmin[i] = the lowest j reaching it,
+ * exceeds[i] = (min_dist[i] > threshold) ? 1 : 0.
+ *
+ *   query         device fp32 [nq][D]; bank device fp32 [n][D].
+ *   nq >= 1; n in 1..PL_MAX_MOTION_BANK; D in 1..65536.
+ *   min_dist      device fp32 [nq]; argmin device int32 [nq]; exceeds device u8 [nq].
+ * The append decision and its cap belong to the caller. */
+pl_status pl_motion_bank_min_l2(const float* query, int32_t nq, const float* bank, int32_t n,
+                                int32_t D, float threshold, float* min_dist, int32_t* argmin,
+                                uint8_t* exceeds, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Latents-pile state machine (host only, no device work)
+ *
+ * PersonaLive, section 流式金字塔去噪: a deque of W windows, oldest at t = 0
+ * and the newest, just enqueued, at the top timestep; each round appends a
+ * window at the top, steps every window one level and pops the oldest after
+ * its t = 0 evaluation, so the queue length is constant.  Section 首帧怎么办:
+ * the queue is pre-filled with W-1 windows of staircase noise so the first
+ * round already emits.
+ *
+ * The pile's device storage is W window slots used as a ring; this struct
+ * tracks which slot holds which window at which t.  A window is evaluated at
+ * t_top, t_top - step_len, ..., 0 in consecutive rounds and is popped after
+ * its t = 0 evaluation (t_top must be a multiple of step_len).
+ * ------------------------------------------------------------------------ */
+typedef struct pl_pile {
+  int32_t W;                       /* slots = windows per forward */
+  int32_t step_len;                /* timestep decrement per round */
+  int32_t t_top;                   /* timestep of a newly enqueued window */
+  int32_t count;                   /* windows currently held */
+  int32_t head;                    /* slot of the oldest held window */
+  int32_t in_round;                /* 1 between begin_round and end_round */
+  int32_t t[PL_MAX_WINDOWS];       /* timestep per slot (valid for held slots) */
+  int64_t id[PL_MAX_WINDOWS];      /* window id per slot, -1 = free */
+  int64_t next_id;                 /* id of the next enqueued window */
+} pl_pile;
+
+/* Initialise.  W in 2..PL_MAX_WINDOWS, step_len >= 1, t_top = (W-1)*step_len.
+ * prefill != 0 places W-1 windows at 0, step_len, ..., (W-2)*step_len in
+ * slots 0..W-2 (ids 0..W-2, oldest first). */
+pl_status pl_pile_init(pl_pile* p, int32_t W, int32_t step_len, int32_t t_top, int32_t prefill);
+
+/* Start a round: enqueue a new window at t_top.
+ *   new_slot  out: slot the new window occupies (the caller fills its latents).
+ *   t_slot    out host int32 [W]: timestep per slot for this round's DDIM step
+ *             (free slots, which exist only without prefill, report t_top and
+ *             hold no window).
+ *   emit_slot out: slot holding the window at t = 0, or -1 if none yet.
+ * PL_EINVAL if a round is already open. */
+pl_status pl_pile_begin_round(pl_pile* p, int32_t* new_slot, int32_t* t_slot, int32_t* emit_slot);
+
+/* Finish the round: pop the window at t = 0 (if any) and step the others down
+ * by step_len.  emitted_id out: the popped window's id or -1.
+ * PL_EINVAL if no round is open. */
+pl_status pl_pile_end_round(pl_pile* p, int64_t* emitted_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PL_H_ */

@@ -8,11 +8,12 @@ draws the seeded synthetic workloads.
 The binding is imported lazily so that ``inputs`` can be used without torch.
 """
 
+import importlib
+
 __all__ = ["binding", "inputs"]
 
 
 def __getattr__(name):
-    if name == "binding":
-        from . import binding
-        return binding
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

@@ -1,0 +1,328 @@
+"""Thin ctypes binding of ``libpl.so`` (declared in ``include/pl.h``).
+
+The raw entry points keep their C names (``pl_refbank_attn``, ...).  The
+tensor helpers below only marshal arguments: they read pointers, strides and
+the current HIP stream from PyTorch tensors and call the library; every step
+of the computation runs in the library's HIP kernels.  There is no fallback:
+if the library is missing or the call fails, an exception is raised.
+
+PyTorch must be imported before the library is loaded so that ``libpl.so``
+binds to the HIP runtime PyTorch already loaded (one runtime per process).
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpl.so")
+
+PL_OK, PL_EINVAL, PL_EUNSUPPORTED, PL_EDEVICE = 0, 1, 2, 3
+PL_MAX_SEGMENTS = 8
+PL_MAX_WINDOWS = 8
+PL_MAX_MOTION_BANK = 4
+
+# every symbol include/pl.h declares
+EXPORTED = (
+    "pl_abi_version",
+    "pl_status_string",
+    "pl_last_error",
+    "pl_refbank_attn_workspace_size",
+    "pl_refbank_attn",
+    "pl_pyramid_ddim_step",
+    "pl_motion_bank_min_l2",
+    "pl_pile_init",
+    "pl_pile_begin_round",
+    "pl_pile_end_round",
+)
+
+
+class PlError(RuntimeError):
+    """A pl_* call returned a non-zero status."""
+
+    def __init__(self, name, status, detail):
+        self.status = status
+        super().__init__(f"{name} failed with {status_name(status)}: {detail}")
+
+
+class pl_kv_segment(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("len", ctypes.c_int64),
+        ("ld", ctypes.c_int64),
+        ("frame_stride", ctypes.c_int64),
+    ]
+
+
+class pl_pile(ctypes.Structure):
+    _fields_ = [
+        ("W", ctypes.c_int32),
+        ("step_len", ctypes.c_int32),
+        ("t_top", ctypes.c_int32),
+        ("count", ctypes.c_int32),
+        ("head", ctypes.c_int32),
+        ("in_round", ctypes.c_int32),
+        ("t", ctypes.c_int32 * PL_MAX_WINDOWS),
+        ("id", ctypes.c_int64 * PL_MAX_WINDOWS),
+        ("next_id", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def load():
+    """Load libpl.so once and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "or python -m streaming_diffusion_portrait_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, f32, f64, vp, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double,
+                                  ctypes.c_void_p, ctypes.c_size_t)
+    lib.pl_abi_version.restype = i32
+    lib.pl_abi_version.argtypes = []
+    lib.pl_status_string.restype = ctypes.c_char_p
+    lib.pl_status_string.argtypes = [i32]
+    lib.pl_last_error.restype = ctypes.c_char_p
+    lib.pl_last_error.argtypes = []
+    lib.pl_refbank_attn_workspace_size.restype = sz
+    lib.pl_refbank_attn_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i64), i32]
+    lib.pl_refbank_attn.restype = i32
+    lib.pl_refbank_attn.argtypes = [vp, i64, i64, vp, i64, i64, i32, i32, i32, i32,
+                                    ctypes.POINTER(pl_kv_segment), i32, f32, vp, sz, vp]
+    lib.pl_pyramid_ddim_step.restype = i32
+    lib.pl_pyramid_ddim_step.argtypes = [vp, vp, vp, vp, i32, i64, ctypes.POINTER(i32), i32,
+                                         ctypes.POINTER(f64), i32, f64, i32, vp]
+    lib.pl_motion_bank_min_l2.restype = i32
+    lib.pl_motion_bank_min_l2.argtypes = [vp, i32, vp, i32, i32, f32, vp, vp, vp, vp]
+    lib.pl_pile_init.restype = i32
+    lib.pl_pile_init.argtypes = [ctypes.POINTER(pl_pile), i32, i32, i32, i32]
+    lib.pl_pile_begin_round.restype = i32
+    lib.pl_pile_begin_round.argtypes = [ctypes.POINTER(pl_pile), ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                        ctypes.POINTER(i32)]
+    lib.pl_pile_end_round.restype = i32
+    lib.pl_pile_end_round.argtypes = [ctypes.POINTER(pl_pile), ctypes.POINTER(i64)]
+    _lib = lib
+    return lib
+
+
+def status_name(status):
+    return load().pl_status_string(int(status)).decode()
+
+
+def last_error():
+    return load().pl_last_error().decode()
+
+
+def _check(name, status):
+    if status != PL_OK:
+        raise PlError(name, status, last_error())
+
+
+# ---- raw entry points, same names as the C ABI ----------------------------------
+def pl_refbank_attn(*args):
+    return load().pl_refbank_attn(*args)
+
+
+def pl_refbank_attn_workspace_size(*args):
+    return load().pl_refbank_attn_workspace_size(*args)
+
+
+def pl_pyramid_ddim_step(*args):
+    return load().pl_pyramid_ddim_step(*args)
+
+
+def pl_motion_bank_min_l2(*args):
+    return load().pl_motion_bank_min_l2(*args)
+
+
+def pl_pile_init(*args):
+    return load().pl_pile_init(*args)
+
+
+def pl_pile_begin_round(*args):
+    return load().pl_pile_begin_round(*args)
+
+
+def pl_pile_end_round(*args):
+    return load().pl_pile_end_round(*args)
+
+
+# ---- tensor helpers ---------------------------------------------------------------
+def _stream_ptr(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _rows(t, name):
+    """(row stride, frame stride) of a [F, L, C] or [L, C] tensor with unit column stride."""
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in its last dimension")
+    if t.dim() == 3:
+        return t.stride(1), t.stride(0)
+    if t.dim() == 2:
+        return t.stride(0), 0
+    raise ValueError(f"{name} must be [F, L, C] or [L, C]")
+
+
+def make_segments(segments):
+    """Segment table for the key axis (the bank segment assembly).
+
+    ``segments``: sequence of ``(k, v)`` fp16 device tensors, either
+    ``[F, Ls, C]`` (per-frame: the frame's own tokens) or ``[Ls, C]`` (shared
+    by every frame: the reference entry and anchors).  Nothing is copied; the
+    table holds pointers and strides.  Returns ``(array, keepalive)``.
+    """
+    n = len(segments)
+    if not 1 <= n <= PL_MAX_SEGMENTS:
+        raise ValueError(f"1..{PL_MAX_SEGMENTS} segments required")
+    arr = (pl_kv_segment * n)()
+    for i, (k, v) in enumerate(segments):
+        _need(k, torch.float16, "k")
+        _need(v, torch.float16, "v")
+        if k.shape != v.shape or k.stride() != v.stride():
+            raise ValueError("k and v of a segment must share shape and strides")
+        ld, fs = _rows(k, "k")
+        arr[i] = pl_kv_segment(k.data_ptr(), v.data_ptr(), k.shape[-2], ld, fs)
+    return arr, segments
+
+
+def refbank_attn(q, segments, heads, out=None, scale=None, stream=None):
+    """O = ref-bank attention of one layer (see ``pl_refbank_attn``).
+
+    ``q``: fp16 device ``[F, L, C]``; ``segments`` as for :func:`make_segments`;
+    ``heads``: H with d = C / H.  Returns ``out`` (allocated if None).
+    """
+    _need(q, torch.float16, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [F, L, C]")
+    F, L, C = q.shape
+    if C % heads:
+        raise ValueError("C must be divisible by heads")
+    d = C // heads
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, torch.float16, "out")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = d ** -0.5
+    q_ld, q_fs = _rows(q, "q")
+    o_ld, o_fs = _rows(out, "out")
+    segs, _keep = make_segments(segments)
+    lens = (ctypes.c_int64 * len(segments))(*[s.len for s in segs])
+    ws = load().pl_refbank_attn_workspace_size(F, L, heads, d, lens, len(segments))
+    if ws:
+        raise RuntimeError("workspace-requiring configuration is not expected here")
+    st = pl_refbank_attn(ctypes.c_void_p(q.data_ptr()), q_ld, q_fs, ctypes.c_void_p(out.data_ptr()), o_ld, o_fs,
+                         F, L, heads, d, segs, len(segments), float(scale), None, 0, _stream_ptr(stream))
+    _check("pl_refbank_attn", st)
+    return out
+
+
+def pyramid_ddim_step(x_t, eps, t_windows, x_prev=None, x0_out=None, emit_window=-1, step_len=333,
+                      alphas_cumprod=None, final_alpha_cumprod=-1.0, stream=None):
+    """Per-window DDIM step over a window-major fp32 pile (see ``pl_pyramid_ddim_step``).
+
+    ``x_t``/``eps``: fp32 device tensors whose leading axis splits into
+    ``W = len(t_windows)`` contiguous windows.  ``x_prev`` may be ``x_t``
+    (in place).  Returns ``(x_prev, x0_out)``.
+    """
+    _need(x_t, torch.float32, "x_t")
+    _need(eps, torch.float32, "eps")
+    if not (x_t.is_contiguous() and eps.is_contiguous()) or x_t.shape != eps.shape:
+        raise ValueError("x_t and eps must be contiguous with equal shapes")
+    W = len(t_windows)
+    if W < 1 or x_t.numel() % W:
+        raise ValueError("the pile must split into W windows")
+    per = x_t.numel() // W
+    if x_prev is None:
+        x_prev = torch.empty_like(x_t)
+    _need(x_prev, torch.float32, "x_prev")
+    if not x_prev.is_contiguous() or x_prev.numel() != x_t.numel():
+        raise ValueError("x_prev must be contiguous with x_t's size")
+    if emit_window >= 0 and x0_out is None:
+        x0_out = torch.empty(per, dtype=torch.float32, device=x_t.device)
+    if x0_out is not None:
+        _need(x0_out, torch.float32, "x0_out")
+        if not x0_out.is_contiguous() or x0_out.numel() != per:
+            raise ValueError("x0_out must be contiguous with one window's size")
+    ts = (ctypes.c_int32 * W)(*[int(t) for t in t_windows])
+    if alphas_cumprod is None:
+        ab_ptr, T = None, 1000
+    else:
+        ab = (ctypes.c_double * len(alphas_cumprod))(*[float(a) for a in alphas_cumprod])
+        ab_ptr, T = ab, len(alphas_cumprod)
+    st = pl_pyramid_ddim_step(ctypes.c_void_p(x_t.data_ptr()), ctypes.c_void_p(eps.data_ptr()),
+                              ctypes.c_void_p(x_prev.data_ptr()),
+                              ctypes.c_void_p(x0_out.data_ptr()) if x0_out is not None else None,
+                              W, per, ts, int(step_len), ab_ptr, T, float(final_alpha_cumprod), int(emit_window),
+                              _stream_ptr(stream))
+    _check("pl_pyramid_ddim_step", st)
+    return x_prev, x0_out
+
+
+def motion_bank_min_l2(query, bank, threshold=17.0, out=None, stream=None):
+    """Minimum L2 distance of each query to the motion bank (see ``pl_motion_bank_min_l2``).
+
+    ``query``: fp32 device ``[nq, D]`` (or ``[D]``); ``bank``: fp32 ``[n, D]``.
+    Returns ``(min_dist fp32 [nq], argmin int32 [nq], exceeds uint8 [nq])``.
+    """
+    _need(query, torch.float32, "query")
+    _need(bank, torch.float32, "bank")
+    if query.dim() == 1:
+        query = query.unsqueeze(0)
+    if not (query.is_contiguous() and bank.is_contiguous()) or query.shape[1] != bank.shape[1]:
+        raise ValueError("query [nq, D] and bank [n, D] must be contiguous and share D")
+    nq, D = query.shape
+    n = bank.shape[0]
+    if out is None:
+        dev = query.device
+        out = (torch.empty(nq, dtype=torch.float32, device=dev), torch.empty(nq, dtype=torch.int32, device=dev),
+               torch.empty(nq, dtype=torch.uint8, device=dev))
+    md, am, ex = out
+    st = pl_motion_bank_min_l2(ctypes.c_void_p(query.data_ptr()), nq, ctypes.c_void_p(bank.data_ptr()), n, D,
+                               float(threshold), ctypes.c_void_p(md.data_ptr()), ctypes.c_void_p(am.data_ptr()),
+                               ctypes.c_void_p(ex.data_ptr()), _stream_ptr(stream))
+    _check("pl_motion_bank_min_l2", st)
+    return md, am, ex
+
+
+class Pile:
+    """Host-side latents-pile state machine backed by ``pl_pile_*``."""
+
+    def __init__(self, W=4, step_len=333, t_top=None, prefill=True):
+        self._p = pl_pile()
+        if t_top is None:
+            t_top = (W - 1) * step_len
+        _check("pl_pile_init", pl_pile_init(ctypes.byref(self._p), W, step_len, t_top, 1 if prefill else 0))
+        self.W = W
+
+    def begin_round(self):
+        """-> (new_slot, t_per_slot list, emit_slot or -1)."""
+        ns, es = ctypes.c_int32(), ctypes.c_int32()
+        ts = (ctypes.c_int32 * self.W)()
+        _check("pl_pile_begin_round", pl_pile_begin_round(ctypes.byref(self._p), ctypes.byref(ns), ts, ctypes.byref(es)))
+        return ns.value, list(ts), es.value
+
+    def end_round(self):
+        """-> id of the popped window or -1."""
+        e = ctypes.c_int64()
+        _check("pl_pile_end_round", pl_pile_end_round(ctypes.byref(self._p), ctypes.byref(e)))
+        return e.value
+
+    def slot_ids(self):
+        return [self._p.id[s] for s in range(self.W)]

@@ -1,0 +1,108 @@
+// Fused per-window DDIM step over the latents pile (HBM-bandwidth bound).
+//
+// PersonaLive write-up, section 流式金字塔去噪: one forward gives every window
+// of the pile its epsilon estimate, every window steps from its own t to
+// t - 333, and the window leaving the queue hands its x0 estimate
+// (pred_original_sample) to the VAE.  The host folds alpha_bar[t] and
+// alpha_bar[t - step] into four fp64 coefficients per window, rounded to fp32:
+//   x_prev = a_w * x_t + b_w * eps,   x0 = c_w * x_t + d_w * eps.
+//
+// One pass: each element of x_t and eps is read once; x_prev is written for
+// every window and x0 only for the emitted one (12 B/element + 4 B per
+// emitted element).  The grid is 2-D: blockIdx.y selects the window, so the
+// coefficients are wave-uniform (scalar registers) and no per-element
+// division is needed.  Loads and stores are 16 B per lane.
+#include "pl_internal.h"
+
+namespace pl {
+namespace {
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+constexpr int kDdimThreads = 256;
+constexpr int kDdimUnroll = 4;  // float4 per thread per grid-stride step
+
+__global__ void __launch_bounds__(kDdimThreads)
+ddim_vec4_kernel(const f4v* x_t, const f4v* eps, f4v* x_prev,
+                 f4v* __restrict__ x0_out, int64_t n4_per_window, int emit_window, DdimLaunch cf) {
+  const int w = blockIdx.y;
+  const float a = cf.a[w], b = cf.b[w], c = cf.c[w], d = cf.d[w];
+  const bool emit = (w == emit_window);
+  const f4v* xw = x_t + (int64_t)w * n4_per_window;
+  const f4v* ew = eps + (int64_t)w * n4_per_window;
+  f4v* pw = x_prev + (int64_t)w * n4_per_window;
+  const int64_t stride = (int64_t)gridDim.x * kDdimThreads * kDdimUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kDdimThreads * kDdimUnroll + threadIdx.x; base < n4_per_window;
+       base += stride) {
+    f4v xv[kDdimUnroll], ev[kDdimUnroll];
+#pragma unroll
+    for (int u = 0; u < kDdimUnroll; ++u) {
+      const int64_t i = base + (int64_t)u * kDdimThreads;
+      if (i < n4_per_window) {
+        xv[u] = __builtin_nontemporal_load(xw + i);
+        ev[u] = __builtin_nontemporal_load(ew + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDdimUnroll; ++u) {
+      const int64_t i = base + (int64_t)u * kDdimThreads;
+      if (i < n4_per_window) {
+        f4v pv;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pv[k] = fmaf(a, xv[u][k], b * ev[u][k]);
+        __builtin_nontemporal_store(pv, pw + i);
+        if (emit) {
+          f4v z;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) z[k] = fmaf(c, xv[u][k], d * ev[u][k]);
+          __builtin_nontemporal_store(z, x0_out + i);
+        }
+      }
+    }
+  }
+}
+
+// Scalar variant for sizes or pointers that do not allow 16 B accesses.
+__global__ void __launch_bounds__(kDdimThreads)
+ddim_scalar_kernel(const float* x_t, const float* eps, float* x_prev,
+                   float* __restrict__ x0_out, int64_t n_per_window, int emit_window, DdimLaunch cf) {
+  const int w = blockIdx.y;
+  const float a = cf.a[w], b = cf.b[w], c = cf.c[w], d = cf.d[w];
+  const bool emit = (w == emit_window);
+  const int64_t off = (int64_t)w * n_per_window;
+  for (int64_t i = (int64_t)blockIdx.x * kDdimThreads + threadIdx.x; i < n_per_window;
+       i += (int64_t)gridDim.x * kDdimThreads) {
+    const float xv = x_t[off + i], ev = eps[off + i];
+    x_prev[off + i] = fmaf(a, xv, b * ev);
+    if (emit) x0_out[i] = fmaf(c, xv, d * ev);
+  }
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+hipError_t launch_pyramid_ddim(const DdimLaunch& a, hipStream_t stream) {
+  const bool vec = (a.elems_per_window % 4 == 0) && aligned16(a.x_t) && aligned16(a.eps) &&
+                   aligned16(a.x_prev) && (a.x0_out == nullptr || aligned16(a.x0_out));
+  // Enough blocks to cover the window in one grid-stride step, capped so a
+  // large pile keeps ~16 blocks per CU resident in total.
+  const int64_t per_block = vec ? (int64_t)kDdimThreads * kDdimUnroll * 4 : (int64_t)kDdimThreads;
+  int64_t bx = (a.elems_per_window + per_block - 1) / per_block;
+  const int64_t cap = (256 * 16 + a.W - 1) / a.W;
+  if (bx > cap) bx = cap;
+  if (bx < 1) bx = 1;
+  dim3 grid((unsigned)bx, (unsigned)a.W);
+  if (vec) {
+    hipLaunchKernelGGL(ddim_vec4_kernel, grid, dim3(kDdimThreads), 0, stream,
+                       reinterpret_cast<const f4v*>(a.x_t), reinterpret_cast<const f4v*>(a.eps),
+                       reinterpret_cast<f4v*>(a.x_prev), reinterpret_cast<f4v*>(a.x0_out),
+                       a.elems_per_window / 4, a.emit_window, a);
+  } else {
+    hipLaunchKernelGGL(ddim_scalar_kernel, grid, dim3(kDdimThreads), 0, stream, a.x_t, a.eps, a.x_prev,
+                       a.x0_out, a.elems_per_window, a.emit_window, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pl

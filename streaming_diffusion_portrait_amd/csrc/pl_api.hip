@@ -1,0 +1,268 @@
+// C-ABI host layer: argument validation, per-window DDIM coefficients, the
+// pile state machine and kernel dispatch.  Every check runs before any HIP
+// call, so an invalid call returns without touching the device.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "pl_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pl_status fail(pl_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+pl_status ok() {
+  g_last_error[0] = '\0';
+  return PL_OK;
+}
+
+pl_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PL_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Stable Diffusion's scaled_linear schedule: beta_i = (s0 + i*(s1-s0)/(T-1))^2
+// with s0 = sqrt(0.00085), s1 = sqrt(0.012), alpha_bar_t = prod_{i<=t}(1 - beta_i).
+struct SdSchedule {
+  double ab[1000];
+  SdSchedule() {
+    const int T = 1000;
+    const double s0 = std::sqrt(0.00085), s1 = std::sqrt(0.012);
+    double prod = 1.0;
+    for (int i = 0; i < T; ++i) {
+      const double r = (i == T - 1) ? s1 : s0 + (s1 - s0) * (double)i / (double)(T - 1);
+      prod *= 1.0 - r * r;
+      ab[i] = prod;
+    }
+  }
+};
+
+const SdSchedule& sd_schedule() {
+  static const SdSchedule s;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pl_abi_version(void) { return PL_ABI_VERSION; }
+
+const char* pl_status_string(pl_status s) {
+  switch (s) {
+    case PL_OK: return "PL_OK";
+    case PL_EINVAL: return "PL_EINVAL";
+    case PL_EUNSUPPORTED: return "PL_EUNSUPPORTED";
+    case PL_EDEVICE: return "PL_EDEVICE";
+    default: return "PL_UNKNOWN";
+  }
+}
+
+const char* pl_last_error(void) { return g_last_error; }
+
+// ---------------------------------------------------------------------------
+size_t pl_refbank_attn_workspace_size(int32_t F, int32_t Lq, int32_t H, int32_t d, const int64_t* seg_len,
+                                      int32_t nseg) {
+  (void)F; (void)Lq; (void)H; (void)d; (void)seg_len; (void)nseg;
+  return 0;
+}
+
+pl_status pl_refbank_attn(const void* q, int64_t q_ld, int64_t q_frame_stride, void* o, int64_t o_ld,
+                          int64_t o_frame_stride, int32_t F, int32_t Lq, int32_t H, int32_t d,
+                          const pl_kv_segment* segs, int32_t nseg, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!q || !o) return fail(PL_EINVAL, "pl_refbank_attn: q and o must be non-null");
+  if (!segs) return fail(PL_EINVAL, "pl_refbank_attn: segs must be non-null");
+  if (F < 1 || Lq < 1 || H < 1) return fail(PL_EINVAL, "pl_refbank_attn: F, Lq, H must be >= 1 (got %d, %d, %d)", F, Lq, H);
+  if (nseg < 1 || nseg > PL_MAX_SEGMENTS)
+    return fail(PL_EINVAL, "pl_refbank_attn: nseg must be in [1, %d] (got %d)", PL_MAX_SEGMENTS, nseg);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PL_EINVAL, "pl_refbank_attn: scale must be finite and > 0");
+  if (d != 32 && d != 40 && d != 80 && d != 160)
+    return fail(PL_EUNSUPPORTED, "pl_refbank_attn: head dim %d not supported (32, 40, 80, 160)", d);
+  const int64_t width = (int64_t)H * d;
+  if (q_ld < width || o_ld < width)
+    return fail(PL_EINVAL, "pl_refbank_attn: q_ld/o_ld must be >= H*d = %lld", (long long)width);
+  if (q_frame_stride < 0 || o_frame_stride < 0) return fail(PL_EINVAL, "pl_refbank_attn: frame strides must be >= 0");
+  if (F > 1 && o_frame_stride < (int64_t)Lq * o_ld)
+    return fail(PL_EINVAL, "pl_refbank_attn: o_frame_stride must be >= Lq*o_ld so frames do not overlap");
+  if (q_ld % 8 || o_ld % 8 || q_frame_stride % 8 || o_frame_stride % 8)
+    return fail(PL_EUNSUPPORTED, "pl_refbank_attn: strides must be multiples of 8 elements");
+  if (!aligned16(q) || !aligned16(o)) return fail(PL_EUNSUPPORTED, "pl_refbank_attn: q and o must be 16-byte aligned");
+  int64_t total = 0;
+  pl::AttnLaunch a;
+  std::memset(&a, 0, sizeof(a));
+  for (int i = 0; i < nseg; ++i) {
+    const pl_kv_segment& s = segs[i];
+    if (!s.k || !s.v) return fail(PL_EINVAL, "pl_refbank_attn: segment %d has a null k or v", i);
+    if (s.len < 1) return fail(PL_EINVAL, "pl_refbank_attn: segment %d has len %lld < 1", i, (long long)s.len);
+    if (s.ld < width) return fail(PL_EINVAL, "pl_refbank_attn: segment %d ld < H*d", i);
+    if (s.frame_stride < 0) return fail(PL_EINVAL, "pl_refbank_attn: segment %d frame_stride < 0", i);
+    if (s.ld % 8 || s.frame_stride % 8)
+      return fail(PL_EUNSUPPORTED, "pl_refbank_attn: segment %d strides must be multiples of 8 elements", i);
+    if (!aligned16(s.k) || !aligned16(s.v))
+      return fail(PL_EUNSUPPORTED, "pl_refbank_attn: segment %d pointers must be 16-byte aligned", i);
+    total += s.len;
+    a.seg[i].k = static_cast<const _Float16*>(s.k);
+    a.seg[i].v = static_cast<const _Float16*>(s.v);
+    a.seg[i].len = s.len;
+    a.seg[i].ld = s.ld;
+    a.seg[i].frame_stride = s.frame_stride;
+  }
+  if (total > (int64_t(1) << 24)) return fail(PL_EINVAL, "pl_refbank_attn: total key length exceeds 2^24");
+  a.q = static_cast<const _Float16*>(q);
+  a.o = static_cast<_Float16*>(o);
+  a.q_ld = q_ld;
+  a.q_frame_stride = q_frame_stride;
+  a.o_ld = o_ld;
+  a.o_frame_stride = o_frame_stride;
+  a.F = F;
+  a.Lq = Lq;
+  a.H = H;
+  a.d = d;
+  a.nseg = nseg;
+  a.scale = scale;
+  return device_status(pl::launch_refbank_attn(a, static_cast<hipStream_t>(stream)), "pl_refbank_attn launch");
+}
+
+// ---------------------------------------------------------------------------
+pl_status pl_pyramid_ddim_step(const float* x_t, const float* eps, float* x_prev, float* x0_out, int32_t W,
+                               int64_t elems_per_window, const int32_t* t_host, int32_t step_len,
+                               const double* alphas_cumprod_host, int32_t T, double final_alpha_cumprod,
+                               int32_t emit_window, void* stream) {
+  if (!x_t || !eps || !x_prev) return fail(PL_EINVAL, "pl_pyramid_ddim_step: x_t, eps, x_prev must be non-null");
+  if (!t_host) return fail(PL_EINVAL, "pl_pyramid_ddim_step: t_host must be non-null");
+  if (W < 1 || W > PL_MAX_WINDOWS)
+    return fail(PL_EINVAL, "pl_pyramid_ddim_step: W must be in [1, %d] (got %d)", PL_MAX_WINDOWS, W);
+  if (elems_per_window < 1) return fail(PL_EINVAL, "pl_pyramid_ddim_step: elems_per_window must be >= 1");
+  if (elems_per_window > (int64_t(1) << 40)) return fail(PL_EINVAL, "pl_pyramid_ddim_step: elems_per_window too large");
+  if (step_len < 1) return fail(PL_EINVAL, "pl_pyramid_ddim_step: step_len must be >= 1");
+  if (emit_window < -1 || emit_window >= W)
+    return fail(PL_EINVAL, "pl_pyramid_ddim_step: emit_window must be -1 or in [0, W) (got %d)", emit_window);
+  if (emit_window >= 0 && !x0_out) return fail(PL_EINVAL, "pl_pyramid_ddim_step: x0_out is required when emitting");
+  const double* ab;
+  if (alphas_cumprod_host) {
+    if (T < 1) return fail(PL_EINVAL, "pl_pyramid_ddim_step: T must be >= 1");
+    ab = alphas_cumprod_host;
+    for (int i = 0; i < T; ++i)
+      if (!(ab[i] > 0.0 && ab[i] <= 1.0))
+        return fail(PL_EINVAL, "pl_pyramid_ddim_step: alphas_cumprod[%d] not in (0, 1]", i);
+  } else {
+    if (T != 1000) return fail(PL_EINVAL, "pl_pyramid_ddim_step: the built-in schedule has T = 1000 (got %d)", T);
+    ab = sd_schedule().ab;
+  }
+  double fin = final_alpha_cumprod;
+  if (fin < 0.0) fin = ab[0];
+  if (!(fin > 0.0 && fin <= 1.0)) return fail(PL_EINVAL, "pl_pyramid_ddim_step: final_alpha_cumprod not in (0, 1]");
+  pl::DdimLaunch a;
+  std::memset(&a, 0, sizeof(a));
+  for (int w = 0; w < W; ++w) {
+    const int t = t_host[w];
+    if (t < 0 || t >= T) return fail(PL_EINVAL, "pl_pyramid_ddim_step: t[%d] = %d not in [0, %d)", w, t, T);
+    const double at = ab[t];
+    const int prev = t - step_len;
+    const double ap = prev >= 0 ? ab[prev] : fin;
+    // x0 = (x_t - sqrt(1-at) eps)/sqrt(at); x_prev = sqrt(ap) x0 + sqrt(1-ap) eps
+    const double c = 1.0 / std::sqrt(at);
+    const double d = -std::sqrt(1.0 - at) / std::sqrt(at);
+    a.a[w] = (float)(std::sqrt(ap) * c);
+    a.b[w] = (float)(std::sqrt(ap) * d + std::sqrt(1.0 - ap));
+    a.c[w] = (float)c;
+    a.d[w] = (float)d;
+  }
+  a.x_t = x_t;
+  a.eps = eps;
+  a.x_prev = x_prev;
+  a.x0_out = emit_window >= 0 ? x0_out : nullptr;
+  a.W = W;
+  a.elems_per_window = elems_per_window;
+  a.emit_window = emit_window;
+  return device_status(pl::launch_pyramid_ddim(a, static_cast<hipStream_t>(stream)), "pl_pyramid_ddim_step launch");
+}
+
+// ---------------------------------------------------------------------------
+pl_status pl_motion_bank_min_l2(const float* query, int32_t nq, const float* bank, int32_t n, int32_t D,
+                                float threshold, float* min_dist, int32_t* argmin, uint8_t* exceeds,
+                                void* stream) {
+  if (!query || !bank || !min_dist || !argmin || !exceeds)
+    return fail(PL_EINVAL, "pl_motion_bank_min_l2: pointers must be non-null");
+  if (nq < 1) return fail(PL_EINVAL, "pl_motion_bank_min_l2: nq must be >= 1 (got %d)", nq);
+  if (n < 1 || n > PL_MAX_MOTION_BANK)
+    return fail(PL_EINVAL, "pl_motion_bank_min_l2: n must be in [1, %d] (got %d)", PL_MAX_MOTION_BANK, n);
+  if (D < 1 || D > 65536) return fail(PL_EINVAL, "pl_motion_bank_min_l2: D must be in [1, 65536] (got %d)", D);
+  if (std::isnan(threshold)) return fail(PL_EINVAL, "pl_motion_bank_min_l2: threshold is NaN");
+  pl::MotionLaunch a{query, bank, nq, n, D, threshold, min_dist, argmin, exceeds};
+  return device_status(pl::launch_motion_min_l2(a, static_cast<hipStream_t>(stream)), "pl_motion_bank_min_l2 launch");
+}
+
+// ---------------------------------------------------------------------------
+pl_status pl_pile_init(pl_pile* p, int32_t W, int32_t step_len, int32_t t_top, int32_t prefill) {
+  if (!p) return fail(PL_EINVAL, "pl_pile_init: p must be non-null");
+  if (W < 2 || W > PL_MAX_WINDOWS) return fail(PL_EINVAL, "pl_pile_init: W must be in [2, %d]", PL_MAX_WINDOWS);
+  if (step_len < 1) return fail(PL_EINVAL, "pl_pile_init: step_len must be >= 1");
+  if (t_top != (W - 1) * step_len)
+    return fail(PL_EINVAL, "pl_pile_init: t_top must equal (W-1)*step_len so a window leaves after W evaluations");
+  std::memset(p, 0, sizeof(*p));
+  p->W = W;
+  p->step_len = step_len;
+  p->t_top = t_top;
+  for (int s = 0; s < PL_MAX_WINDOWS; ++s) {
+    p->id[s] = -1;
+    p->t[s] = t_top;
+  }
+  if (prefill) {
+    // staircase: slot s holds the s-th oldest window at t = s * step_len
+    for (int s = 0; s < W - 1; ++s) {
+      p->id[s] = p->next_id++;
+      p->t[s] = s * step_len;
+    }
+    p->count = W - 1;
+  }
+  return ok();
+}
+
+pl_status pl_pile_begin_round(pl_pile* p, int32_t* new_slot, int32_t* t_slot, int32_t* emit_slot) {
+  if (!p || !new_slot || !t_slot || !emit_slot) return fail(PL_EINVAL, "pl_pile_begin_round: null argument");
+  if (p->in_round) return fail(PL_EINVAL, "pl_pile_begin_round: a round is already open");
+  if (p->count >= p->W) return fail(PL_EINVAL, "pl_pile_begin_round: pile is full");
+  const int slot = (p->head + p->count) % p->W;
+  p->id[slot] = p->next_id++;
+  p->t[slot] = p->t_top;
+  p->count += 1;
+  p->in_round = 1;
+  *new_slot = slot;
+  *emit_slot = -1;
+  for (int s = 0; s < p->W; ++s) t_slot[s] = p->id[s] >= 0 ? p->t[s] : p->t_top;
+  if (p->t[p->head] == 0 && p->id[p->head] >= 0) *emit_slot = p->head;
+  return ok();
+}
+
+pl_status pl_pile_end_round(pl_pile* p, int64_t* emitted_id) {
+  if (!p || !emitted_id) return fail(PL_EINVAL, "pl_pile_end_round: null argument");
+  if (!p->in_round) return fail(PL_EINVAL, "pl_pile_end_round: no round is open");
+  *emitted_id = -1;
+  if (p->count > 0 && p->t[p->head] == 0) {
+    *emitted_id = p->id[p->head];
+    p->id[p->head] = -1;
+    p->t[p->head] = p->t_top;
+    p->head = (p->head + 1) % p->W;
+    p->count -= 1;
+  }
+  for (int k = 0; k < p->count; ++k) p->t[(p->head + k) % p->W] -= p->step_len;
+  p->in_round = 0;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal interface between the C-ABI host layer (pl_api.hip) and the
+// kernel translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pl.h"
+
+namespace pl {
+
+// ---- reference-bank attention ---------------------------------------------
+struct AttnSegment {
+  const _Float16* k;
+  const _Float16* v;
+  int64_t len;
+  int64_t ld;
+  int64_t frame_stride;
+};
+
+struct AttnLaunch {
+  const _Float16* q;
+  _Float16* o;
+  int64_t q_ld, q_frame_stride;
+  int64_t o_ld, o_frame_stride;
+  int32_t F, Lq, H, d;
+  int32_t nseg;
+  AttnSegment seg[PL_MAX_SEGMENTS];
+  float scale;
+};
+
+// Launch the flash-style MFMA attention for one layer on `stream`.
+hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream);
+
+// ---- pyramid DDIM -------------------------------------------------------------
+struct DdimLaunch {
+  const float* x_t;
+  const float* eps;
+  float* x_prev;
+  float* x0_out;      // nullptr when no window is emitted
+  int32_t W;
+  int64_t elems_per_window;
+  int32_t emit_window;  // -1 = none
+  // per-window coefficients: x_prev = a*x_t + b*eps, x0 = c*x_t + d*eps
+  float a[PL_MAX_WINDOWS], b[PL_MAX_WINDOWS], c[PL_MAX_WINDOWS], d[PL_MAX_WINDOWS];
+};
+
+hipError_t launch_pyramid_ddim(const DdimLaunch& a, hipStream_t stream);
+
+// ---- motion-bank min-L2 -------------------------------------------------------
+struct MotionLaunch {
+  const float* query;
+  const float* bank;
+  int32_t nq, n, D;
+  float threshold;
+  float* min_dist;
+  int32_t* argmin;
+  uint8_t* exceeds;
+};
+
+hipError_t launch_motion_min_l2(const MotionLaunch& a, hipStream_t stream);
+
+}  // namespace pl

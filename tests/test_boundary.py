@@ -1,0 +1,186 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+rejects invalid arguments before touching the device, and its host-side pile
+state machine matches the oracle's queue.
+
+No call here reaches a kernel launch: every call has an argument that
+validation rejects, and validation runs before any HIP call.  The fake device
+addresses below are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from streaming_diffusion_portrait_amd import binding as B
+from oracle import PyramidPile
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "pl.h")
+
+A = ctypes.c_void_p(0x10000)        # fake, 16-byte aligned "device" address
+A2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)      # fake, 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libpl.so not built")
+    return B.load()
+
+
+def declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pl_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(B.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.pl_abi_version() == 1
+    assert [B.status_name(s) for s in range(4)] == ["PL_OK", "PL_EINVAL", "PL_EUNSUPPORTED", "PL_EDEVICE"]
+    assert B.status_name(99) == "PL_UNKNOWN"
+
+
+def _segs(*specs):
+    arr = (B.pl_kv_segment * max(1, len(specs)))()
+    for i, (k, v, ln, ld, fs) in enumerate(specs):
+        arr[i] = B.pl_kv_segment(k, v, ln, ld, fs)
+    return arr
+
+
+def _attn(q=A, q_ld=64, q_fs=64 * 256, o=A2, o_ld=64, o_fs=64 * 256, F=16, L=256, H=2, d=32, segs=None, nseg=1,
+          scale=0.17):
+    if segs is None:
+        segs = _segs((A, A2, 256, 64, 0))
+    return B.pl_refbank_attn(q, q_ld, q_fs, o, o_ld, o_fs, F, L, H, d, segs, nseg, scale, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), B.PL_EINVAL),
+    (dict(o=None), B.PL_EINVAL),
+    (dict(F=0), B.PL_EINVAL),
+    (dict(L=0), B.PL_EINVAL),
+    (dict(H=0), B.PL_EINVAL),
+    (dict(nseg=0), B.PL_EINVAL),
+    (dict(nseg=9), B.PL_EINVAL),
+    (dict(scale=0.0), B.PL_EINVAL),
+    (dict(scale=float("nan")), B.PL_EINVAL),
+    (dict(d=64, q_ld=128, o_ld=128), B.PL_EUNSUPPORTED),
+    (dict(d=48, q_ld=96, o_ld=96), B.PL_EUNSUPPORTED),
+    (dict(q_ld=32), B.PL_EINVAL),
+    (dict(q_ld=68), B.PL_EUNSUPPORTED),
+    (dict(q=MIS), B.PL_EUNSUPPORTED),
+    (dict(o_fs=64 * 100), B.PL_EINVAL),
+    (dict(segs=_segs((A, A2, 0, 64, 0))), B.PL_EINVAL),
+    (dict(segs=_segs((None, A2, 16, 64, 0))), B.PL_EINVAL),
+    (dict(segs=_segs((A, A2, 16, 48, 0))), B.PL_EINVAL),
+    (dict(segs=_segs((A, A2, 16, 64, 12))), B.PL_EUNSUPPORTED),
+    (dict(segs=_segs((A, MIS, 16, 64, 0))), B.PL_EUNSUPPORTED),
+    (dict(segs=_segs((A, A2, 16, 64, -64))), B.PL_EINVAL),
+    (dict(segs=_segs((A, A2, 1 << 24, 64, 0), (A, A2, 1, 64, 0)), nseg=2), B.PL_EINVAL),
+])
+def test_attention_rejects(lib, kw, status):
+    assert _attn(**kw) == status
+    assert B.last_error() != ""
+
+
+def test_attention_second_segment_checked(lib):
+    segs = _segs((A, A2, 256, 64, 0), (A, A2, 0, 64, 0))
+    assert _attn(segs=segs, nseg=2) == B.PL_EINVAL
+    assert "segment 1" in B.last_error()
+
+
+def test_workspace_size_is_zero(lib):
+    lens = (ctypes.c_int64 * 2)(4096, 4096)
+    assert lib.pl_refbank_attn_workspace_size(16, 4096, 8, 40, lens, 2) == 0
+
+
+def _ddim(x=A, e=A, xp=A2, x0=A, W=4, n=256, t=(999, 666, 333, 0), step=333, ab=None, T=1000, fin=-1.0, emit=3):
+    ts = (ctypes.c_int32 * max(1, len(t)))(*t)
+    return B.pl_pyramid_ddim_step(x, e, xp, x0, W, n, ts, step, ab, T, fin, emit, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(e=None), dict(xp=None), dict(W=0), dict(W=9), dict(n=0), dict(step=0),
+    dict(t=(999, 666, 333, 1000)), dict(t=(999, 666, 333, -1)), dict(emit=4), dict(emit=-2),
+    dict(x0=None), dict(T=999), dict(fin=1.5),
+])
+def test_ddim_rejects(lib, kw):
+    assert _ddim(**kw) == B.PL_EINVAL
+    assert B.last_error() != ""
+
+
+def test_ddim_rejects_bad_schedule(lib):
+    ab = (ctypes.c_double * 3)(0.9, 0.0, 0.5)
+    assert _ddim(t=(2, 1, 0, 0), ab=ab, T=3) == B.PL_EINVAL
+    assert "alphas_cumprod[1]" in B.last_error()
+
+
+@pytest.mark.parametrize("kw", [
+    dict(nq=0), dict(n=0), dict(n=5), dict(D=0), dict(D=65537), dict(q=None), dict(ex=None),
+    dict(thr=float("nan")),
+])
+def test_motion_rejects(lib, kw):
+    args = dict(q=A, nq=1, b=A2, n=4, D=512, thr=17.0, md=A, am=A, ex=A)
+    args.update(kw)
+    st = B.pl_motion_bank_min_l2(args["q"], args["nq"], args["b"], args["n"], args["D"], args["thr"], args["md"],
+                                 args["am"], args["ex"], None)
+    assert st == B.PL_EINVAL
+
+
+def test_last_error_clears_after_success(lib):
+    p = B.pl_pile()
+    assert B.pl_pile_init(ctypes.byref(p), 1, 333, 0, 1) == B.PL_EINVAL
+    assert B.last_error() != ""
+    assert B.pl_pile_init(ctypes.byref(p), 4, 333, 999, 1) == B.PL_OK
+    assert B.last_error() == ""
+
+
+def test_pile_rejects(lib):
+    p = B.pl_pile()
+    assert B.pl_pile_init(ctypes.byref(p), 4, 333, 998, 1) == B.PL_EINVAL
+    assert B.pl_pile_init(ctypes.byref(p), 9, 333, 8 * 333, 1) == B.PL_EINVAL
+    assert B.pl_pile_init(ctypes.byref(p), 4, 0, 0, 1) == B.PL_EINVAL
+    assert B.pl_pile_init(ctypes.byref(p), 4, 333, 999, 1) == B.PL_OK
+    e = ctypes.c_int64()
+    assert B.pl_pile_end_round(ctypes.byref(p), ctypes.byref(e)) == B.PL_EINVAL
+    pile = B.Pile()
+    pile.begin_round()
+    with pytest.raises(B.PlError):
+        pile.begin_round()
+
+
+@pytest.mark.parametrize("prefill", [True, False])
+def test_pile_matches_oracle_queue(lib, prefill, pages_constants):
+    ts = pages_constants["timesteps"]
+    W = pages_constants["windows"]
+    pile = B.Pile(W, pages_constants["step_length"], prefill=prefill)
+    ref = PyramidPile(ts, pages_constants["frames_per_window"], prefill=prefill)
+    slot_of = {wid: s for s, wid in enumerate(pile.slot_ids()) if wid >= 0}
+    for r in range(14):
+        new_slot, t_slot, emit_slot = pile.begin_round()
+        ids = pile.slot_ids()
+        evaluated, emitted = ref.round()
+        assert ids[new_slot] == evaluated[-1][0]
+        slot_of[ids[new_slot]] = new_slot
+        # every held window sits in its slot at the oracle's timestep
+        for wid, t in evaluated:
+            assert t_slot[slot_of[wid]] == t
+        held = {wid for wid, _ in evaluated}
+        assert {i for i in ids if i >= 0} == held
+        if emitted is None:
+            assert emit_slot == -1
+        else:
+            assert emit_slot == slot_of[emitted] and t_slot[emit_slot] == 0
+        assert pile.end_round() == (-1 if emitted is None else emitted)

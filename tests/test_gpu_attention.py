@@ -1,0 +1,201 @@
+"""GPU parity of pl_refbank_attn against the fp64 oracle.
+
+Small cases are compared element by element over the whole output; they span
+several query and key tiles with ragged tails and every supported head
+dimension.  The workload shapes (tiny, top 64^2, mid 32^2, low 16^2 / 8^2)
+run at full size in the launch configuration the bench uses and are compared
+on seeded samples of (frame, head, row) that the oracle computes one by one.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+
+from oracle import refbank_attention
+from streaming_diffusion_portrait_amd import inputs
+from _helpers import assert_attn_close, attn_errors, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from streaming_diffusion_portrait_amd import binding
+    binding.load()
+    return binding
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_gpu(B, q, segs, H, scale=None):
+    """segs: list of (k, v, shared) numpy fp16 arrays -> GPU output as numpy fp16."""
+    dq = dev(q)
+    dsegs = [(dev(k), dev(v)) for k, v, _ in segs]
+    out = B.refbank_attn(dq, dsegs, H, scale=scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def rand16(rng, *shape, gain=1.0):
+    return (rng.standard_normal(shape, dtype=np.float32) * np.float32(gain)).astype(np.float16)
+
+
+SMALL = [
+    # (name, d, F, L, H, [(len, shared)], gain)
+    ("d40 ragged NT1", 40, 3, 300, 2, [(300, False), (100, True), (37, True)], 1.0),
+    ("d40 ragged NT4", 40, 2, 1100, 1, [(1100, False), (130, True)], 1.0),
+    ("d40 peaky", 40, 2, 200, 2, [(200, False), (200, True)], 4.0),
+    ("d80 ragged NT1", 80, 2, 130, 2, [(130, False), (64, True), (65, True), (1, True)], 1.0),
+    ("d80 ragged NT2", 80, 2, 1030, 1, [(1030, False), (70, True)], 1.0),
+    ("d160 ragged NT1", 160, 2, 70, 2, [(70, False), (33, True)], 1.0),
+    ("d160 ragged NT2", 160, 1, 1025, 1, [(1025, False), (31, True), (32, True)], 1.0),
+    ("d32 ragged", 32, 2, 257, 2, [(257, False), (256, True), (5, True)], 1.0),
+    ("d32 NT4", 32, 1, 1024, 2, [(1024, False), (1024, True)], 1.0),
+    ("single key", 40, 2, 64, 2, [(1, False)], 1.0),
+    ("bank only", 80, 3, 50, 1, [(77, True)], 1.0),
+]
+
+
+@pytest.mark.parametrize("name,d,F,L,H,segspec,gain", SMALL, ids=[s[0] for s in SMALL])
+def test_small_full_compare(B, name, d, F, L, H, segspec, gain):
+    say("attn", name)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    C = H * d
+    q = rand16(rng, F, L, C, gain=gain)
+    segs = []
+    for ln, shared in segspec:
+        shape = (ln, C) if shared else (F, ln, C)
+        segs.append((rand16(rng, *shape), rand16(rng, *shape), shared))
+    got = run_gpu(B, q, segs, H)
+    ref = refbank_attention(q, segs, H)
+    e = assert_attn_close(got, ref, name)
+    assert e["norm_rel"] <= 2e-3, e
+
+
+def test_strided_views_of_fused_qkv(B):
+    say("attn strided qkv views")
+    rng = np.random.default_rng(5)
+    F, L, H, d = 2, 200, 2, 40
+    C = H * d
+    qkv = dev(rand16(rng, F, L, 3 * C))
+    bank = dev(rand16(rng, 90, 2 * C))
+    q, k, v = qkv[..., :C], qkv[..., C:2 * C], qkv[..., 2 * C:]
+    bk, bv = bank[:, :C], bank[:, C:]
+    out = torch.zeros(F, L + 3, C + 8, dtype=torch.float16, device="cuda")[:, :L, :C]
+    B.refbank_attn(q, [(k, v), (bk, bv)], H, out=out)
+    torch.cuda.synchronize()
+    h = lambda t: t.cpu().numpy()
+    ref = refbank_attention(h(q), [(h(k), h(v), False), (h(bk), h(bv), True)], H)
+    assert_attn_close(h(out), ref, "strided")
+
+
+def test_segment_order_does_not_matter(B):
+    say("attn segment order")
+    rng = np.random.default_rng(6)
+    F, L, H, d = 2, 150, 2, 40
+    C = H * d
+    q = rand16(rng, F, L, C)
+    segs = [(rand16(rng, F, L, C), rand16(rng, F, L, C), False),
+            (rand16(rng, 90, C), rand16(rng, 90, C), True),
+            (rand16(rng, 60, C), rand16(rng, 60, C), True)]
+    a = run_gpu(B, q, segs, H)
+    b = run_gpu(B, q, [segs[2], segs[0], segs[1]], H)
+    ref = refbank_attention(q, segs, H)
+    assert_attn_close(a, ref, "order a")
+    assert_attn_close(b, ref, "order b")
+
+
+def test_deterministic(B):
+    say("attn determinism")
+    lay = inputs.attention_layer(11, 4, 1024, 320, 1)
+    segs = [(lay["k_self"], lay["v_self"], False)] + [(k, v, True) for k, v in zip(lay["bank_k"], lay["bank_v"])]
+    a = run_gpu(B, lay["q"], segs, 8)
+    b = run_gpu(B, lay["q"], segs, 8)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def _sampled_check(B, name, seed, F, L, C, H, m, n_pairs=6, n_rows=96):
+    say("attn", name, f"F={F} L={L} C={C} H={H} m={m}")
+    lay = inputs.attention_layer(seed, F, L, C, m)
+    segs = [(lay["k_self"], lay["v_self"], False)] + [(k, v, True) for k, v in zip(lay["bank_k"], lay["bank_v"])]
+    got = run_gpu(B, lay["q"], segs, H)
+    assert np.all(np.isfinite(got))
+    d = C // H
+    rng = np.random.default_rng(seed + 1000)
+    pairs = {(int(rng.integers(F)), int(rng.integers(H))) for _ in range(n_pairs)}
+    pairs |= {(0, 0), (F - 1, H - 1)}
+    worst = None
+    for f, h in sorted(pairs):
+        rows = np.unique(np.concatenate([rng.choice(L, size=min(n_rows, L), replace=False), [0, L - 1]]))
+        ref = refbank_attention(lay["q"], segs, H, frames=[f], head_list=[h], rows=rows)[(f, h)]
+        e = assert_attn_close(got[f][rows][:, h * d:(h + 1) * d], ref, f"{name} f={f} h={h}")
+        worst = e if worst is None or e["max_abs"] > worst["max_abs"] else worst
+    say("attn", name, "worst", worst)
+    return got
+
+
+def test_config_tiny_full(B):
+    say("attn tiny full")
+    lay = inputs.attention_layer(0, 16, 256, 64, 0)
+    segs = [(lay["k_self"], lay["v_self"], False), (lay["bank_k"][0], lay["bank_v"][0], True)]
+    got = run_gpu(B, lay["q"], segs, 2)
+    ref = refbank_attention(lay["q"], segs, 2)
+    assert_attn_close(got, ref, "tiny")
+
+
+def test_config_top(B):
+    _sampled_check(B, "top 64^2 d40", 1, 16, 4096, 320, 8, 0)
+
+
+def test_config_top_stress_peaky(B):
+    say("attn top peaky")
+    lay = inputs.attention_layer(21, 16, 4096, 320, 0, q_gain=4.0)
+    segs = [(lay["k_self"], lay["v_self"], False), (lay["bank_k"][0], lay["bank_v"][0], True)]
+    got = run_gpu(B, lay["q"], segs, 8)
+    rows = np.arange(0, 4096, 97)
+    for f, h in [(0, 0), (7, 3), (15, 7)]:
+        ref = refbank_attention(lay["q"], segs, 8, frames=[f], head_list=[h], rows=rows)[(f, h)]
+        assert_attn_close(got[f][rows][:, h * 40:(h + 1) * 40], ref, f"peaky f={f} h={h}")
+
+
+def test_config_mid(B):
+    _sampled_check(B, "mid 32^2 d80 m3", 2, 16, 1024, 640, 8, 3)
+
+
+def test_config_low_256(B):
+    _sampled_check(B, "low 16^2 d160 m3", 3, 16, 256, 1280, 8, 3)
+
+
+def test_config_low_64_full(B):
+    say("attn low 8^2 full")
+    lay = inputs.attention_layer(3, 16, 64, 1280, 3)
+    segs = [(lay["k_self"], lay["v_self"], False)] + [(k, v, True) for k, v in zip(lay["bank_k"], lay["bank_v"])]
+    got = run_gpu(B, lay["q"], segs, 8)
+    ref = refbank_attention(lay["q"], segs, 8)
+    assert_attn_close(got, ref, "low 8^2")
+
+
+def test_max_bank_top_level(B):
+    # the largest key axis of the round: 64^2 with three anchors (Lk = 20480)
+    _sampled_check(B, "top 64^2 d40 m3", 31, 16, 4096, 320, 8, 3, n_pairs=3, n_rows=48)
+
+
+def test_zero_queries_mean_of_values_at_scale(B):
+    # property that holds at any size: Q = 0 gives the mean of all values
+    say("attn zero q property")
+    lay = inputs.attention_layer(41, 2, 4096, 320, 1)
+    q = np.zeros_like(lay["q"])
+    segs = [(lay["k_self"], lay["v_self"], False)] + [(k, v, True) for k, v in zip(lay["bank_k"], lay["bank_v"])]
+    got = run_gpu(B, q, segs, 8)
+    for f in range(2):
+        vals = np.concatenate([lay["v_self"][f].astype(np.float64)] + [v.astype(np.float64) for v in lay["bank_v"]])
+        mean = vals.mean(axis=0)
+        err = np.abs(got[f].astype(np.float64) - mean[None, :])
+        assert err.max() <= 1e-2 and err.mean() <= 1e-3, (err.max(), err.mean())
