@@ -1,0 +1,339 @@
+"""Benchmark of the streaming pyramid's hot path on one MI355X.
+
+One step is one pyramid round at 512x512 on the device: the 16 reference-bank
+spatial self-attention layers of the SD1.5 denoiser (16 frames, 8 heads,
+frame tokens + reference + m anchors as keys, fp16), the fused per-window DDIM
+step over the 16x4x64x64 fp32 latents pile with the leaving window's x0, and
+the 512-d motion-bank min-L2 check.  Inputs are seeded synthetic tensors
+already resident in HBM; every launch goes through the C ABI (libpl.so).
+
+Prints ONE JSON line on stdout.  Everything else goes to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+The ``cpu_baseline`` leg times the fp64 CPU oracle on a bounded sample of the
+same workload (a few (frame, head) pairs of the first 64^2 layer); it is a
+reported baseline, not the target.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# Published MI355X figures: fp16 dense MFMA 2.5 PFLOP/s, HBM3E 8 TB/s.
+PEAK_FP16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+FRAMES_OUT_PER_ROUND = 4      # one window of 4 frames leaves per round
+SEED = 4                      # seed of the full-round workload
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--m", type=int, default=None, help="anchors per round (default: one seeded draw)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the DDIM bandwidth sweep")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="after timing, run one plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def attention_flops(F, L, C, lk):
+    """Algorithmic FLOPs of one layer: QK^T and PV, 2 flops per MAC each."""
+    return 4 * F * L * lk * C
+
+
+def attention_bytes(F, L, C, m):
+    """Compulsory HBM bytes of one layer: Q, K_self, V_self, O plus the shared bank, fp16."""
+    return (4 * F * L * C + 2 * (1 + m) * L * C) * 2
+
+
+def traffic_record(kernel_key):
+    """Measured HBM bytes per launch for a kernel, from the committed counter summary.
+
+    The summary names the kernel source hash it was taken on; when the
+    source has changed since, the figure no longer applies and None is
+    returned.
+    """
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    src = os.path.join(ROOT, "streaming_diffusion_portrait_amd", "csrc", "attn.hip")
+    if not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    with open(src, "rb") as fh:
+        h = hashlib.sha256(fh.read()).hexdigest()[:16]
+    for line in open(path, encoding="utf-8"):
+        # | key | source sha256[:16] | bytes per launch | ...
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 3 and cells[0] == kernel_key and cells[1] == h:
+            try:
+                return float(cells[2])
+            except ValueError:
+                return None
+    return None
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("this benchmark runs on exactly one GPU: the streaming round's work is one GPU's share "
+            "(frame sharding across GPUs is a design note only); run with --gpus 1")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from streaming_diffusion_portrait_amd import binding as B, inputs
+
+    if not torch.cuda.is_available():
+        log("no GPU visible: bench.py needs an MI355X")
+        sys.exit(1)
+    B.load()  # raises if libpl.so is missing: there is no other path
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs {props.multi_processor_count}")
+
+    m = inputs.round_m(SEED) if args.m is None else int(args.m)
+    F, H = 16, 8
+    todev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---- inputs: fresh seeded tensors per layer -------------------------------------------------
+    t0 = time.perf_counter()
+    layers = []
+    for li, (name, L, C) in enumerate(inputs.SD15_LAYERS):
+        lay = inputs.attention_layer(1000 * SEED + li, F, L, C, m)
+        q = todev(lay["q"])
+        segs = [(todev(lay["k_self"]), todev(lay["v_self"]))]
+        segs += [(todev(k), todev(v)) for k, v in zip(lay["bank_k"], lay["bank_v"])]
+        out = torch.empty_like(q)
+        call = B.PreparedAttn(q, segs, H, out)
+        lk = L * (2 + m)
+        layers.append(dict(name=name, L=L, C=C, d=C // H, lk=lk, q=q, segs=segs, out=out, call=call,
+                           host=lay if li == 0 else None,
+                           flops=attention_flops(F, L, C, lk), bytes=attention_bytes(F, L, C, m)))
+    x_t_np, eps_np = inputs.ddim_pile(SEED, (16, 4, 64, 64))
+    x_t, eps = todev(x_t_np), todev(eps_np)
+    x_prev = torch.empty_like(x_t)
+    x0 = torch.empty((4, 4, 64, 64), dtype=torch.float32, device=dev)
+    n_bank = 1 + m
+    bank_np, q_np, _ = inputs.motion_bank(SEED, n_bank, 512, nq=1)
+    mb, mq = todev(bank_np), todev(q_np)
+    md = (torch.empty(1, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
+          torch.empty(1, dtype=torch.uint8, device=dev))
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f}s (m={m})")
+
+    pile = B.Pile(4, 333)
+
+    def step(events=None):
+        # the round's 16 attention layers, then the DDIM step and the drift check
+        for li, lay in enumerate(layers):
+            if events is not None:
+                events[li][0].record()
+            lay["call"]()
+            if events is not None:
+                events[li][1].record()
+        _, t_slot, emit = pile.begin_round()
+        B.pyramid_ddim_step(x_t, eps, t_slot, x_prev=x_prev, x0_out=x0, emit_window=emit)
+        pile.end_round()
+        B.motion_bank_min_l2(mq, mb, 17.0, out=md)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole rounds ----------------------------------------------------------
+    K = args.steps
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in layers]
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(K):
+        step(evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = 1e3 * elapsed / K
+
+    per_layer_ms = [float(np.mean([evs[k][li][0].elapsed_time(evs[k][li][1]) for k in range(K)]))
+                    for li in range(len(layers))]
+    round_flops = sum(l["flops"] for l in layers)
+    attn_ms = sum(per_layer_ms)
+    tflops_round = round_flops / (ms_per_step * 1e-3) / 1e12
+    frames_per_s = FRAMES_OUT_PER_ROUND / (ms_per_step * 1e-3)
+
+    # dominant kernel: the d=40 (64^2 level) attention launches, 87% of the round's FLOPs at m=0
+    dom = [li for li, l in enumerate(layers) if l["d"] == 40]
+    dom_ms = float(np.mean([per_layer_ms[li] for li in dom]))
+    dom_flops = layers[dom[0]]["flops"]
+    dom_tflops = dom_flops / (dom_ms * 1e-3) / 1e12
+    traffic = traffic_record(f"attn_d40_L4096_m{m}")
+
+    layer_report = [dict(layer=l["name"], L=l["L"], C=l["C"], d=l["d"], keys=l["lk"],
+                         us=round(1e3 * per_layer_ms[li], 2),
+                         tflops=round(l["flops"] / (per_layer_ms[li] * 1e-3) / 1e12, 1),
+                         pct_fp16_peak=round(100 * l["flops"] / (per_layer_ms[li] * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 1))
+                    for li, l in enumerate(layers)]
+    for r in layer_report:
+        log(f"  {r['layer']:>4} L={r['L']:5d} d={r['d']:3d} keys={r['keys']:5d}  {r['us']:9.2f} us  "
+            f"{r['tflops']:7.1f} TFLOP/s  {r['pct_fp16_peak']:5.1f}%")
+
+    # ---- DDIM and motion at the round's shapes (separately timed, same kernels) ---------------
+    def time_it(fn, n=200):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3  # us per call (includes launch gaps)
+
+    t_slot = [0, 333, 666, 999]
+    ddim_us = time_it(lambda: B.pyramid_ddim_step(x_t, eps, t_slot, x_prev=x_prev, x0_out=x0, emit_window=0))
+    motion_us = time_it(lambda: B.motion_bank_min_l2(mq, mb, 17.0, out=md))
+
+    # ---- DDIM bandwidth sweep: rotating working sets well beyond the 256 MB cache ------------
+    sweep = None
+    if not args.no_sweep:
+        per_window = 16 * 1024 * 1024  # elements; 4 windows -> 256 MiB per tensor
+        sets = []
+        for s in range(2):
+            a = torch.randn(4 * per_window, device=dev)
+            e = torch.randn(4 * per_window, device=dev)
+            sets.append((a, e, torch.empty_like(a), torch.empty(per_window, device=dev)))
+        sweep_bytes = 4 * per_window * 12 + per_window * 4
+        ts = [999, 666, 333, 0]
+        for s in sets:
+            B.pyramid_ddim_step(s[0], s[1], ts, x_prev=s[2], x0_out=s[3], emit_window=3)
+        torch.cuda.synchronize()
+        reps = 20
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for r in range(reps):
+            s = sets[r % 2]
+            B.pyramid_ddim_step(s[0], s[1], ts, x_prev=s[2], x0_out=s[3], emit_window=3)
+        b.record()
+        torch.cuda.synchronize()
+        sw_us = a.elapsed_time(b) / reps * 1e3
+        gbs = sweep_bytes / (sw_us * 1e-6) / 1e9
+        sweep = dict(bytes_per_call=sweep_bytes, working_set_bytes=2 * (4 * per_window * 12 + per_window * 4),
+                     us=round(sw_us, 1), GBps=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 3))
+        del sets
+        log(f"  DDIM sweep: {sweep_bytes / 2**20:.0f} MiB per call, {sw_us:.1f} us, {gbs:.0f} GB/s "
+            f"({100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s)")
+
+    if args.copy_calib:
+        # a plain device copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB): the yardstick
+        # that scales the FETCH_SIZE / WRITE_SIZE counters into bytes
+        src = torch.empty(2**28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- CPU baseline: the oracle on a bounded sample -------------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(layers[0], F, H, m)
+
+    dom_l = layers[dom[0]]
+    result = {
+        "metric": "ref-bank attn TFLOP/s (% fp16 MFMA peak) + pyramid-step frames/s on 1 MI355X",
+        "value": round(tflops_round, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"full pyramid round at 512x512: 16 SD1.5 reference-bank attention layers "
+                         f"(16 frames, 8 heads, keys = own tokens + reference + {m} anchors), fused DDIM on "
+                         f"a 16x4x64x64 fp32 pile at t=999/666/333/0, motion-bank min-L2 512-d vs {n_bank} entries"),
+            "frames": F, "windows": 4, "heads": H, "m": m, "layers": len(layers), "resolution": 512,
+        },
+        "pct_fp16_peak": round(100 * tflops_round / PEAK_FP16_TFLOPS, 2),
+        "frames_per_s": round(frames_per_s, 1),
+        "attn_ms_per_round": round(attn_ms, 4),
+        "round_attn_tflop": round(round_flops / 1e12, 4),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": f"refbank_attn d=40 (64^2 level: F=16, L=4096, C=320, keys={dom_l['lk']})",
+            "achieved": round(dom_tflops, 2),
+            "peak": PEAK_FP16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(dom_tflops / PEAK_FP16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": dom_flops,
+            "algorithmic_bytes_per_launch": dom_l["bytes"],
+            "avg_launch_us": round(1e3 * dom_ms, 2),
+        },
+        "ddim": {"us_at_round_shape": round(ddim_us, 2), "bytes_at_round_shape": 3407872, "sweep": sweep},
+        "motion_us": round(motion_us, 2),
+        "layers": layer_report,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(lay0, F, H, m):
+    """Time the fp64 oracle on a sample of the first 64^2 layer and compare it with the GPU output."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    host = lay0["host"]
+    segs = [(host["k_self"], host["v_self"], False)]
+    segs += [(k, v, True) for k, v in zip(host["bank_k"], host["bank_v"])]
+    got = lay0["out"].cpu().numpy()
+    L, C = lay0["L"], lay0["C"]
+    d = C // H
+    lk = lay0["lk"]
+    pairs_done, flops, err_max = 0, 0, 0.0
+    budget_s, t0 = 12.0, time.perf_counter()
+    rng = np.random.default_rng(0)
+    order = rng.permutation(F * H)
+    for idx in order:
+        f, h = divmod(int(idx), H)
+        ref = oracle.refbank_attention(host["q"], segs, H, frames=[f], head_list=[h])[(f, h)]
+        pairs_done += 1
+        flops += 4 * L * lk * d
+        err_max = max(err_max, float(np.abs(got[f][:, h * d:(h + 1) * d].astype(np.float64) - ref).max()))
+        if time.perf_counter() - t0 > budget_s:
+            break
+    sec = time.perf_counter() - t0
+    log(f"  cpu oracle: {pairs_done} (frame, head) pairs in {sec:.1f}s on {threads} threads, "
+        f"max|gpu - oracle| {err_max:.2e}")
+    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{pairs_done} of {F * H} (frame, head) pairs of the first 64^2 layer "
+                       f"(L=4096, d={d}, keys={lk}), fp64 NumPy, {sec:.1f} s"),
+            "seconds": round(sec, 2), "max_abs_err_gpu_vs_oracle": err_max}
+
+
+if __name__ == "__main__":
+    main()

@@ -326,3 +326,42 @@ class Pile:
 
     def slot_ids(self):
         return [self._p.id[s] for s in range(self.W)]
+
+
+class PreparedAttn:
+    """A pl_refbank_attn call with its arguments marshalled once.
+
+    For a streaming loop that attends the same buffers every round: calling
+    the object only crosses into the library (one ctypes call), so per-launch
+    host cost stays far below the small layers' GPU time.  The tensors must
+    stay alive and unchanged in shape while the object is used; ``stream``
+    is fixed at preparation (default: the current stream then).
+    """
+
+    def __init__(self, q, segments, heads, out, scale=None, stream=None):
+        _need(q, torch.float16, "q")
+        _need(out, torch.float16, "out")
+        if q.dim() != 3 or out.shape != q.shape:
+            raise ValueError("q and out must be [F, L, C] of the same shape")
+        F, L, C = q.shape
+        if C % heads:
+            raise ValueError("C must be divisible by heads")
+        d = C // heads
+        if scale is None:
+            scale = d ** -0.5
+        q_ld, q_fs = _rows(q, "q")
+        o_ld, o_fs = _rows(out, "out")
+        self._segs, self._keep = make_segments(segments)
+        self._tensors = (q, out)
+        lens = (ctypes.c_int64 * len(segments))(*[s.len for s in self._segs])
+        if load().pl_refbank_attn_workspace_size(F, L, heads, d, lens, len(segments)):
+            raise RuntimeError("workspace-requiring configuration is not expected here")
+        self.args = (ctypes.c_void_p(q.data_ptr()), q_ld, q_fs, ctypes.c_void_p(out.data_ptr()), o_ld, o_fs,
+                     F, L, heads, d, self._segs, len(segments), float(scale), None, 0, _stream_ptr(stream))
+        self.flops = 4 * F * L * sum(s.len for s in self._segs) * C
+        self._fn = load().pl_refbank_attn
+
+    def __call__(self):
+        st = self._fn(*self.args)
+        if st != PL_OK:
+            raise PlError("pl_refbank_attn", st, last_error())
