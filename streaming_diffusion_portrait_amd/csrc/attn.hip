@@ -9,20 +9,21 @@
 //
 // Work decomposition
 //   * one workgroup = 4 wavefronts = one (head, frame, query tile); each wave
-//     owns NQB blocks of 32 query rows;
-//   * K and V tiles of BN keys are copied HBM -> LDS by the direct-to-LDS
+//     owns NQB blocks of 32 query rows (the K/V operands read from LDS serve
+//     all of them, which keeps LDS traffic per score low);
+//   * K and V tiles of BN = 32*NKB keys are copied HBM -> LDS by direct-to-LDS
 //     loads (global_load_lds_dwordx4), row-major exactly as they sit in HBM
-//     (2*d bytes per key), double buffered: the copy of tile i+1 is in flight
-//     while tile i is consumed; one barrier per tile;
+//     (2*d bytes per key), into a ring of NBUF buffers that runs up to NBUF-1
+//     tiles ahead of the tile being consumed; one barrier per tile;
 //   * workgroup ids are remapped so that each of the 8 XCDs (ids are dealt
 //     round-robin to them) works on a contiguous range of (head, frame, tile),
 //     i.e. mostly on one head, whose shared bank keys then stay in its L2.
 //
 // Matrix-core mapping
 //   S^T = K Q^T   v_mfma_f32_32x32x16_f16: A = 32 keys x 16 d from LDS,
-//                 B = Q^T for 32 queries held in registers for the whole
-//                 kernel.  Lane l ends up with the scores of query l%32 for
-//                 16 of the 32 keys (4 runs of 4 consecutive keys).
+//                 B = Q^T for 32 queries, held in registers for the whole
+//                 kernel.  Lane l ends up with the scores of query l%32
+//                 for 16 of the 32 keys (4 runs of 4 consecutive keys).
 //   O^T = V^T P^T v_mfma_f32_16x16x32_f16: B = P^T is assembled from the S^T
 //                 registers of two query halves with v_permlane16_swap, so
 //                 probabilities never touch LDS; A = V^T is read from the
@@ -31,20 +32,26 @@
 //                 lists the keys fixes which V rows each transposing read
 //                 fetches (vrow() below).
 //
+// Software pipeline (fast tiles, per wave, 32-key blocks b): iteration b
+// evaluates softmax(b+1) on the vector ALU, O^T += V^T(b) P^T(b) and
+// S^T(b+2) = K(b+2) Q^T on the matrix core -- three independent streams that
+// are interleaved instruction by instruction, so the exponentials and
+// conversions issue while the matrix products execute.
+//
 // Softmax (fp32, log2 units).  Q is pre-scaled by scale*log2(e) and rounded
 // to fp16 once, so the matrix core yields s = scale*log2(e)*q.k directly.
-//   * Exact tiles: the row maximum of the tile is taken, and the running
-//     offset m is raised when the tile maximum exceeds it by more than 8
-//     (then p <= 2^8 always, safe in fp16); the accumulator is rescaled then.
-//   * Fast tiles: after the first tile the offset is frozen at that tile's
-//     maximum and no per-element maximum is taken at all.  For a head dim
-//     that leaves a zero-padded column (d = 40), the padding carries the
-//     offset into the matrix core: K gets a column of ones and Q the value -m,
-//     so s - m comes out of the MFMA and p = exp2 of the accumulator.
-//     A fast tile would only go wrong if a later score exceeded the frozen
-//     offset by 16 or more (p beyond the fp16 range): the row sum then turns
-//     inf/NaN, which is checked once at the end; the workgroup then recomputes
-//     everything with exact tiles.
+//   * Exact tiles (the first tile; every tile of an exact pass): the block's
+//     row maximum is taken; the running offset m is raised when the maximum
+//     exceeds it by more than 8 (so p <= 2^8, safe in fp16) and the
+//     accumulator is rescaled then.
+//   * Fast tiles: after the first tile the offset is frozen and no maximum is
+//     taken.  For a head dim that leaves a zero-padded column (d = 40), the
+//     padding carries the offset into the matrix core: K gets a column of
+//     ones and Q the value -m, so s - m comes out of the MFMA and p = exp2 of
+//     the accumulator.  A frozen offset only fails if a later score exceeds
+//     it by 16 or more (p beyond the fp16 range): a row sum then turns
+//     inf/NaN, which is checked once at the end; the workgroup then
+//     recomputes everything with exact tiles.
 //   * Row sums come from the same fp16 values that weight V: through the
 //     matrix core (a row of ones in the V^T padding, d = 40) or with
 //     v_dot2_f32_f16 on the packed probabilities (other head dims).
@@ -57,16 +64,20 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef short s4 __attribute__((ext_vector_type(4)));
+typedef short s2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
-
+typedef __attribute__((address_space(3))) s4 lds_s4;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleSlack = 8.0f;  // log2 units a tile max may exceed the running offset by
+constexpr float kRescaleSlack = 8.0f;      // log2 units a block max may exceed the running offset by
 constexpr float kFastMaxOffset = 1024.0f;  // |m| bound for freezing the offset in fp16
+
+// sched_group_barrier instruction classes
+constexpr int kSchedMfma = 0x008, kSchedValu = 0x002, kSchedDsRead = 0x100;
 
 // Key rows (within a 32-key block) fetched by the two transposing reads of
 // lane group g (lanes 16g..16g+15) for the V^T operand.  They follow from the
@@ -76,12 +87,14 @@ constexpr float kFastMaxOffset = 1024.0f;  // |m| bound for freezing the offset 
 // for e >= 4, with vrow(g) = 0, 8, 4, 12 for g = 0..3.
 __device__ __forceinline__ int vrow(int g) { return 8 * (g & 1) + 4 * (g >> 1); }
 
-template <int D_, int NQB_, int NKB_, int MINB_>
+template <int D_, int NQB_, int NKB_, int NBUF_, int MINB_, bool PIPE_>
 struct Cfg {
   static constexpr int D = D_;
-  static constexpr int MINB = MINB_;          // workgroups per CU the register budget is sized for
   static constexpr int NQB = NQB_;            // 32-query blocks per wave
+  static constexpr bool PIPE = PIPE_;         // software-pipelined fast tiles
   static constexpr int NKB = NKB_;            // 32-key blocks per tile
+  static constexpr int NBUF = NBUF_;          // LDS tile buffers in the ring
+  static constexpr int MINB = MINB_;          // workgroups per CU the register budget is sized for
   static constexpr int BN = 32 * NKB;         // keys per tile
   static constexpr int QWG = 32 * NQB * kWaves;  // query rows per workgroup
   static constexpr int KST = (D + 15) / 16;   // 16-wide contraction steps of S^T
@@ -91,12 +104,15 @@ struct Cfg {
   static constexpr int TILEB = BN * ROWB;     // bytes of one K (or V) tile
   static constexpr int CPR = D / 8;           // 16-byte chunks per key row
   static constexpr int LI = BN * CPR / 64;    // wave-wide 16-byte load instructions per tile (K or V)
-  static constexpr int NI = (2 * LI + kWaves - 1) / kWaves;  // load instructions per wave per tile
+  static constexpr int NI = (2 * LI + kWaves - 1) / kWaves;  // load instructions per wave per tile (max)
   static constexpr int BUFB = 2 * TILEB;      // K tile + V tile
-  static constexpr int LDSB = 2 * BUFB + 128; // two buffers + slack read past the last row
+  static constexpr int CONSTB = NBUF * BUFB;  // 16-byte constant chunk (1, 0, ..., 0) in fp16
+  static constexpr int LDSB = CONSTB + 128;   // ring + constant + slack read past the last row
   static_assert(D % 8 == 0, "head dim must be a multiple of 8");
   static_assert(!ONES || D % 16 == 8, "the ones column must start the upper half of the last step");
   static_assert((BN * CPR) % 64 == 0, "a tile must be whole wave-wide load instructions");
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2 to 4 buffers");
+  static_assert(NI * (NBUF - 1) <= 24, "vmcnt wait table range");
 };
 
 struct KParams {
@@ -113,42 +129,72 @@ __device__ __forceinline__ unsigned pack_h2(float a, float b) {
   return __builtin_bit_cast(unsigned, v);
 }
 
-// Round x up to an fp16-representable value (m must not be exceeded by the
-// scores of the tile that defined it).
+// Round x up to an fp16-representable value (the offset must not be exceeded
+// by the scores of the block that defined it).
 __device__ __forceinline__ float round_up_half(float x) {
   _Float16 hx = (_Float16)(x + fabsf(x) * 0.0009765625f);
   float r = (float)hx;
-  return r < x ? x : r;  // never below x (guard; unreachable for |x| <= 1024)
+  return r < x ? x : r;
 }
 
-// Issue this wave's share of the direct-to-LDS copies of one K/V tile.
-// (M0 is named as clobbered by the asm below; nothing else in this kernel
-// keeps a value in it.)
+// Wait until at most n of this wave's vector-memory operations are in flight
+// (n <= 0: all of them; n above the table waits for more than asked, which is safe).
+#define PL_VMCNT_CASE(k) \
+  case k:                \
+    asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); \
+    break;
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    PL_VMCNT_CASE(1) PL_VMCNT_CASE(2) PL_VMCNT_CASE(3) PL_VMCNT_CASE(4) PL_VMCNT_CASE(5) PL_VMCNT_CASE(6)
+    PL_VMCNT_CASE(7) PL_VMCNT_CASE(8) PL_VMCNT_CASE(9) PL_VMCNT_CASE(10) PL_VMCNT_CASE(11) PL_VMCNT_CASE(12)
+    PL_VMCNT_CASE(13) PL_VMCNT_CASE(14) PL_VMCNT_CASE(15) PL_VMCNT_CASE(16) PL_VMCNT_CASE(17) PL_VMCNT_CASE(18)
+    PL_VMCNT_CASE(19) PL_VMCNT_CASE(20) PL_VMCNT_CASE(21) PL_VMCNT_CASE(22) PL_VMCNT_CASE(23) PL_VMCNT_CASE(24)
+    default:
+      if (n > 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      break;
+  }
+}
+#undef PL_VMCNT_CASE
+
+// The copy side of the ring: which tile comes next and this wave's share of
+// each tile's copy instructions.
+template <class C>
+struct Copier {
+  int s;           // segment of the next tile to copy
+  int64_t off;     // its first key within the segment
+  int issued;      // tiles copied so far
+  int ni;          // copy instructions this wave issues per tile
+  int row[C::NI];  // per lane: key row (within the tile) and 16-byte chunk of each instruction
+  int ch[C::NI];
+};
+
+// Issue this wave's share of the direct-to-LDS copies of the next tile and
+// advance.  (M0 is named as clobbered by the asm below; nothing else in this
+// kernel keeps a value in it.)
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 template <class C>
-__device__ __forceinline__ void issue_tile(const KParams& p, char* buf, int s, int64_t off, int f, int h, int wave,
-                                           int lane) {
-  const AttnSegment& sg = p.seg[s];
-  const int64_t valid = sg.len - off;  // >= 1
-  const int64_t base = (int64_t)f * sg.frame_stride + off * sg.ld + (int64_t)h * C::D;
-  const _Float16* kbase = sg.k + base;
-  const _Float16* vbase = sg.v + base;
-  const int64_t ld = sg.ld;
+__device__ __forceinline__ void issue_tile(const KParams& p, char* smem, Copier<C>& cp, int f, int h, int wave) {
+  const AttnSegment& sg = p.seg[cp.s];
+  const int64_t valid = sg.len - cp.off;  // >= 1
+  const int64_t base = (int64_t)f * sg.frame_stride + cp.off * sg.ld + (int64_t)h * C::D;
+  const char* kbase = reinterpret_cast<const char*>(sg.k + base);
+  const char* vbase = reinterpret_cast<const char*>(sg.v + base);
+  const int ld2 = (int)(sg.ld * 2);
+  char* buf = smem + (cp.issued % C::NBUF) * C::BUFB;
 #pragma unroll
   for (int j = 0; j < C::NI; ++j) {
     const int u = wave + kWaves * j;  // wave-uniform
     if (u < 2 * C::LI) {
       const bool isv = u >= C::LI;
       const int uu = isv ? u - C::LI : u;
-      const int c = uu * 64 + lane;
-      int row = c / C::CPR;
-      const int ch = c - row * C::CPR;
+      int row = cp.row[j];
       if (row >= valid) row = (int)valid - 1;  // ragged tail: duplicate a valid row (masked later)
-      const _Float16* src = (isv ? vbase : kbase) + (int64_t)row * ld + ch * 8;
+      const char* src = (isv ? vbase : kbase) + (row * ld2 + cp.ch[j] * 16);
       const char* dst = buf + (isv ? C::TILEB : 0) + uu * 1024;
       // Lane i's 16 bytes land at M0 + 16*i.  Written as asm so the compiler
-      // does not serialise the LDS reads of the other buffer behind this
+      // does not serialise the LDS reads of the other buffers behind this
       // copy; completion is awaited explicitly (vmcnt) before the barrier
       // that publishes the tile.  The instruction has no register result.
       const unsigned m0 = __builtin_amdgcn_readfirstlane(
@@ -159,153 +205,235 @@ __device__ __forceinline__ void issue_tile(const KParams& p, char* buf, int s, i
                    : "memory", "m0");
     }
   }
+  cp.off += C::BN;
+  if (cp.off >= sg.len) {
+    cp.s += 1;
+    cp.off = 0;
+  }
+  cp.issued += 1;
 }
 #pragma clang diagnostic pop
 
-// One K/V tile for one wave.  FAST: offset frozen (no tile maximum).
-// FIRST: the first tile of a pass (sets the offset from its own maximum).
-template <class C, bool FAST>
-__device__ __forceinline__ void tile_step(const char* kt, const h8 (&qf)[C::NQB][C::KST], f4 (&oacc)[C::NQB][2][C::NDT],
-                                          float (&mrun)[C::NQB], float (&lsum)[C::NQB], bool first, int valid,
-                                          int lane, int h, int c16, int g, const u4& kones, const u4& vsel_const,
-                                          bool vsel_data, int krow_off, const int (&vrow_off)[2]) {
-  const char* vt = kt + C::TILEB;
+// Per-wave register state.
+template <class C>
+struct WaveState {
+  h8 qf[C::NQB][C::KST];       // Q^T operands (scaled, fp16)
+  f4 oacc[C::NQB][2][C::NDT];  // O^T accumulators: [query block][16-query half][16-row d tile]
+  float mrun[C::NQB];          // running offset of query l%32 of each block
+  float lsum[C::NQB];          // partial row sums (S layout), when not through the matrix core
+};
 
-  // ---- S^T = K Q^T for the tile ----
-  f16v sacc[C::NQB][C::NKB];
+// Lane constants.
+struct LaneCtx {
+  int lane, h, c16, g;
+  int krow_off;      // K operand LDS byte offset within a 32-key block
+  int vrow_off[2];   // V^T operand LDS byte offsets of the two transposing reads
+  bool kconst;       // this lane's last K step is the constant (ones column) chunk
+  bool vconst;       // this lane's last V^T reads are constant chunks (rows >= D)
+  int vconst_off;    // ... at this LDS byte address
+};
+
+// S^T(block) = K(block) Q^T for every query block of the wave.
+template <class C>
+__device__ __forceinline__ void qk_block(const char* smem, int kblk, const WaveState<C>& ws, const LaneCtx& lc,
+                                         f16v (&sacc)[C::NQB]) {
+  h8 ka[C::KST];
 #pragma unroll
-  for (int kb = 0; kb < C::NKB; ++kb) {
-    h8 ka[C::KST];
+  for (int st = 0; st < C::KST; ++st) {
+    int a = kblk + lc.krow_off + 32 * st;
+    if (C::ONES && st == C::KST - 1) a = lc.kconst ? C::CONSTB : a;
+    ka[st] = *reinterpret_cast<const h8*>(smem + a);
+  }
 #pragma unroll
-    for (int st = 0; st < C::KST; ++st)
-      ka[st] = *reinterpret_cast<const h8*>(kt + krow_off + kb * 32 * C::ROWB + 32 * st);
-    if (C::ONES) {
-      u4 t = __builtin_bit_cast(u4, ka[C::KST - 1]);
+  for (int qb = 0; qb < C::NQB; ++qb) {
+    f16v acc = {};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) t[e] = h ? kones[e] : t[e];
-      ka[C::KST - 1] = __builtin_bit_cast(h8, t);
+    for (int st = 0; st < C::KST; ++st) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[st], ws.qf[qb][st], acc, 0, 0, 0);
+    sacc[qb] = acc;
+  }
+}
+
+// V^T operands of one 32-key block.
+template <class C>
+__device__ __forceinline__ void load_vt(const char* smem, int vblk, const LaneCtx& lc, h8 (&va)[C::NDT]) {
+#pragma unroll
+  for (int t = 0; t < C::NDT; ++t) {
+    int a0 = vblk + 32 * t + lc.vrow_off[0];
+    int a1 = vblk + 32 * t + lc.vrow_off[1];
+    if (C::ONES && t == C::NDT - 1) {
+      a0 = lc.vconst ? lc.vconst_off : a0;
+      a1 = lc.vconst ? lc.vconst_off : a1;
     }
+    const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(smem + a0));
+    const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(smem + a1));
+    u4 w;
+    w[0] = __builtin_bit_cast(unsigned, (s2){lo[0], lo[1]});
+    w[1] = __builtin_bit_cast(unsigned, (s2){lo[2], lo[3]});
+    w[2] = __builtin_bit_cast(unsigned, (s2){hi[0], hi[1]});
+    w[3] = __builtin_bit_cast(unsigned, (s2){hi[2], hi[3]});
+    va[t] = __builtin_bit_cast(h8, w);
+  }
+}
+
+// O^T += V^T P^T for one 32-key block.
+template <class C>
+__device__ __forceinline__ void pv_block(const h8 (&va)[C::NDT], const h8 (&pb)[C::NQB][2], WaveState<C>& ws) {
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
-      f16v a = {};
+  for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
-      for (int st = 0; st < C::KST; ++st) a = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[st], qf[qb][st], a, 0, 0, 0);
-      sacc[qb][kb] = a;
+    for (int t = 0; t < C::NDT; ++t)
+#pragma unroll
+      for (int grp = 0; grp < 2; ++grp)
+        ws.oacc[qb][grp][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t], pb[qb][grp], ws.oacc[qb][grp][t], 0, 0, 0);
+}
+
+// Softmax of one 32-key block: S^T -> P^T operands; keys at or beyond
+// `valid` get no weight.  EXACT: take the block maximum and update the
+// offsets (FIRST: set them from this block).  When an offset moves,
+// `rescale` is set and alpha (S layout) holds the factors the accumulated
+// products of earlier blocks must be multiplied by (the caller applies
+// them); the partial row sums are rescaled here.
+template <class C, bool EXACT>
+__device__ __forceinline__ void softmax_block(f16v (&sacc)[C::NQB], WaveState<C>& ws, const LaneCtx& lc, int valid,
+                                              bool first, h8 (&pb)[C::NQB][2], float (&alpha)[C::NQB], bool& rescale) {
+  if (valid < 32) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * lc.h + (r & 3);
+      if (key >= valid)
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) sacc[qb][r] = -INFINITY;
     }
   }
-
-  // ---- ragged tail: keys at or beyond `valid` get no weight ----
-  if (valid < C::BN) {
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (key >= valid)
-#pragma unroll
-          for (int qb = 0; qb < C::NQB; ++qb) sacc[qb][kb][r] = -INFINITY;
-      }
-  }
-
-  // ---- exact tiles: tile maximum and lazy rescale of the running offset ----
-  if (!FAST) {
-    float mnew[C::NQB], alpha[C::NQB];
-    bool need = first;
+  rescale = false;
+  if (EXACT) {
+    float mx[C::NQB];
+    bool need = false;
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
-      float mx = -INFINITY;
+      float v = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (first) {
-        mnew[qb] = (C::ONES && fabsf(mx) <= kFastMaxOffset) ? round_up_half(mx) : mx;
-        alpha[qb] = 0.f;  // accumulators are still zero
-      } else {
-        need |= (mx > mrun[qb] + kRescaleSlack);
-        mnew[qb] = fmaxf(mrun[qb], mx);
-        alpha[qb] = __builtin_amdgcn_exp2f(mrun[qb] - mnew[qb]);
-      }
+      for (int r = 0; r < 16; ++r) v = fmaxf(v, sacc[qb][r]);
+      mx[qb] = fmaxf(v, __shfl_xor(v, 32, 64));
+      need |= mx[qb] > ws.mrun[qb] + kRescaleSlack;
     }
-    if (__any(need)) {
+    if (first) {
+      rescale = true;
 #pragma unroll
       for (int qb = 0; qb < C::NQB; ++qb) {
-        mrun[qb] = mnew[qb];
-        lsum[qb] *= alpha[qb];
+        ws.mrun[qb] = (C::ONES && fabsf(mx[qb]) <= kFastMaxOffset) ? round_up_half(mx[qb]) : mx[qb];
+        alpha[qb] = 0.f;  // nothing accumulated yet
+      }
+    } else if (__any(need)) {
+      rescale = true;
 #pragma unroll
-        for (int grp = 0; grp < 2; ++grp) {
-          const float a = __shfl(alpha[qb], 16 * grp + c16, 64);
-#pragma unroll
-          for (int t = 0; t < C::NDT; ++t) oacc[qb][grp][t] *= a;
-        }
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        const float mnew = fmaxf(ws.mrun[qb], mx[qb]);
+        alpha[qb] = __builtin_amdgcn_exp2f(ws.mrun[qb] - mnew);
+        ws.mrun[qb] = mnew;
+        ws.lsum[qb] *= alpha[qb];
       }
     }
   }
-  if (!FAST || !C::ONES) {
+  if (EXACT || !C::ONES) {
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[qb][kb][r] -= mrun[qb];
+      for (int r = 0; r < 16; ++r) sacc[qb][r] -= ws.mrun[qb];
   }
-
-  // ---- P = exp2(S - m), P^T operands, O^T += V^T P^T ----
 #pragma unroll
-  for (int kb = 0; kb < C::NKB; ++kb) {
-    h8 va[C::NDT];
+  for (int qb = 0; qb < C::NQB; ++qb) {
+    unsigned pk[4][2];
 #pragma unroll
-    for (int t = 0; t < C::NDT; ++t) {
-      const char* vb = vt + kb * 32 * C::ROWB + 32 * t;
-      const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(vb + vrow_off[0]));
-      const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(vb + vrow_off[1]));
-      u4 w;
-      w[0] = __builtin_bit_cast(unsigned, (short __attribute__((ext_vector_type(2)))){lo[0], lo[1]});
-      w[1] = __builtin_bit_cast(unsigned, (short __attribute__((ext_vector_type(2)))){lo[2], lo[3]});
-      w[2] = __builtin_bit_cast(unsigned, (short __attribute__((ext_vector_type(2)))){hi[0], hi[1]});
-      w[3] = __builtin_bit_cast(unsigned, (short __attribute__((ext_vector_type(2)))){hi[2], hi[3]});
-      if (C::ONES && t == C::NDT - 1) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = vsel_data ? w[e] : vsel_const[e];
-      }
-      va[t] = __builtin_bit_cast(h8, w);
-    }
-#pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
-      unsigned pk[4][2];
+      for (int x = 0; x < 2; ++x)
+        pk[i][x] = pack_h2(__builtin_amdgcn_exp2f(sacc[qb][4 * i + 2 * x]),
+                           __builtin_amdgcn_exp2f(sacc[qb][4 * i + 2 * x + 1]));
+    if (!C::ONES) {
+      const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int x = 0; x < 2; ++x)
-          pk[i][x] = pack_h2(__builtin_amdgcn_exp2f(sacc[qb][kb][4 * i + 2 * x]),
-                             __builtin_amdgcn_exp2f(sacc[qb][kb][4 * i + 2 * x + 1]));
-      if (!C::ONES) {
-        const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int x = 0; x < 2; ++x)
-            lsum[qb] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pk[i][x]), one2, lsum[qb], false);
-      }
-      u4 b0, b1;  // P^T for queries 0..15 and 16..31 of the block
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const auto s01 = __builtin_amdgcn_permlane16_swap(pk[0][x], pk[1][x], false, false);
-        const auto s23 = __builtin_amdgcn_permlane16_swap(pk[2][x], pk[3][x], false, false);
-        b0[x] = s01[0];
-        b1[x] = s01[1];
-        b0[2 + x] = s23[0];
-        b1[2 + x] = s23[1];
-      }
-      const h8 bq0 = __builtin_bit_cast(h8, b0), bq1 = __builtin_bit_cast(h8, b1);
-#pragma unroll
-      for (int t = 0; t < C::NDT; ++t) {
-        oacc[qb][0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t], bq0, oacc[qb][0][t], 0, 0, 0);
-        oacc[qb][1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t], bq1, oacc[qb][1][t], 0, 0, 0);
-      }
+          ws.lsum[qb] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pk[i][x]), one2, ws.lsum[qb], false);
     }
+    u4 b0, b1;  // P^T for queries 0..15 and 16..31 of the block
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const auto s01 = __builtin_amdgcn_permlane16_swap(pk[0][x], pk[1][x], false, false);
+      const auto s23 = __builtin_amdgcn_permlane16_swap(pk[2][x], pk[3][x], false, false);
+      b0[x] = s01[0];
+      b1[x] = s01[1];
+      b0[2 + x] = s23[0];
+      b1[2 + x] = s23[1];
+    }
+    pb[qb][0] = __builtin_bit_cast(h8, b0);
+    pb[qb][1] = __builtin_bit_cast(h8, b1);
   }
+}
+
+// O^T *= alpha (alpha given in S layout, moved to the O^T layout).
+template <class C>
+__device__ __forceinline__ void rescale_acc(WaveState<C>& ws, const LaneCtx& lc, const float (&alpha)[C::NQB]) {
+#pragma unroll
+  for (int qb = 0; qb < C::NQB; ++qb)
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+      const float a = __shfl(alpha[qb], 16 * grp + lc.c16, 64);
+#pragma unroll
+      for (int t = 0; t < C::NDT; ++t) ws.oacc[qb][grp][t] *= a;
+    }
+}
+
+// One tile, blocks in sequence (exact tiles, and fast tiles outside the pipeline).
+template <class C, bool FAST>
+__device__ __forceinline__ void tile_step(const char* smem, int kt, int valid, bool first, WaveState<C>& ws,
+                                          const LaneCtx& lc) {
+#pragma unroll
+  for (int kb = 0; kb < C::NKB; ++kb) {
+    f16v s[C::NQB];
+    qk_block<C>(smem, kt + kb * 32 * C::ROWB, ws, lc, s);
+    h8 va[C::NDT];
+    load_vt<C>(smem, kt + C::TILEB + kb * 32 * C::ROWB, lc, va);
+    h8 pb[C::NQB][2];
+    float alpha[C::NQB];
+    bool resc;
+    softmax_block<C, !FAST>(s, ws, lc, valid - 32 * kb, first && kb == 0, pb, alpha, resc);
+    if (!FAST && resc) rescale_acc<C>(ws, lc, alpha);  // O^T holds only earlier blocks here
+    pv_block<C>(va, pb, ws);
+  }
+}
+
+// Interleave hint for one pipelined iteration: LDS operand reads first, then
+// the softmax's vector work threaded between the matrix products.
+template <class C>
+__device__ __forceinline__ void sched_iteration() {
+  constexpr int nds = C::KST + 2 * C::NDT;
+  constexpr int nmfma = C::NQB * (C::KST + 2 * C::NDT);
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, nds, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+#pragma unroll
+  for (int i = 0; i < nmfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
+  }
+}
+
+// One pipelined iteration over full blocks: softmax(b+1) [s_in -> p_out],
+// O^T += V^T(b) P^T(b) [p_in], S^T(b+2) [-> s_out].
+template <class C>
+__device__ __forceinline__ void pipe_iteration(const char* smem, int vblk, int kblk_next, f16v (&s_in)[C::NQB],
+                                               f16v (&s_out)[C::NQB], const h8 (&p_in)[C::NQB][2],
+                                               h8 (&p_out)[C::NQB][2], WaveState<C>& ws, const LaneCtx& lc) {
+  float alpha[C::NQB];
+  bool resc;
+  h8 va[C::NDT];
+  load_vt<C>(smem, vblk, lc, va);
+  softmax_block<C, false>(s_in, ws, lc, 32, false, p_out, alpha, resc);
+  pv_block<C>(va, p_in, ws);
+  qk_block<C>(smem, kblk_next, ws, lc, s_out);
+  sched_iteration<C>();
 }
 
 template <class C>
@@ -314,9 +442,13 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
   __shared__ int flags[kWaves];
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int h = lane >> 5, c32 = lane & 31;   // 32x32 layout: lane half, query column
-  const int g = lane >> 4, c16 = lane & 15;   // 16x16 layout: row group, column
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  LaneCtx lc;
+  lc.lane = tid & 63;
+  lc.h = lc.lane >> 5;
+  lc.c16 = lc.lane & 15;
+  lc.g = lc.lane >> 4;
+  const int c32 = lc.lane & 31;
 
   // XCD-aware remap of the workgroup id onto (head, frame, query tile).
   const int total = p.nqt * p.F * p.H;
@@ -328,8 +460,8 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
   const int qt = rem - f * p.nqt;
   const int qrow0 = qt * C::QWG + wave * 32 * C::NQB;
 
+  WaveState<C> ws;
   // Q^T operands: Q * scale * log2(e) rounded to fp16, zero beyond d and beyond Lq.
-  h8 qf[C::NQB][C::KST];
   {
     const _Float16* qb_ = p.q + (int64_t)f * p.q_fs + (int64_t)hd * C::D;
 #pragma unroll
@@ -337,93 +469,159 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
       const int row = qrow0 + 32 * qb + c32;
 #pragma unroll
       for (int st = 0; st < C::KST; ++st) {
-        const int col = 16 * st + 8 * h;
+        const int col = 16 * st + 8 * lc.h;
         h8 v = {0, 0, 0, 0, 0, 0, 0, 0};
         if (row < p.Lq && col < C::D) {
           const h8 x = *reinterpret_cast<const h8*>(qb_ + (int64_t)row * p.q_ld + col);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = (_Float16)((float)x[e] * p.c2);
         }
-        qf[qb][st] = v;
+        ws.qf[qb][st] = v;
       }
     }
   }
 
-  // Constant operand parts for the padding column D (used when C::ONES):
-  // K columns D..D+7 = (1, 0, ..., 0); V^T rows D.. = ones at row D, zeros below.
-  u4 kones = {0u, 0u, 0u, 0u}, vsel_const = {0u, 0u, 0u, 0u};
-  kones[0] = pack_h2(1.0f, 0.0f);
-  const int vrow_in_tile = C::ONES ? (16 * (C::NDT - 1) + c16) : 0;  // d row of this lane in the last V^T tile
-  const bool vsel_data = vrow_in_tile < C::D;
-  if (vrow_in_tile == C::D) {
+  // The constant chunk (1, 0, ..., 0) used for the padding column D.
+  if (tid < 8) reinterpret_cast<_Float16*>(smem + C::CONSTB)[tid] = (_Float16)(tid == 0 ? 1.0f : 0.0f);
+  lc.kconst = C::ONES && lc.h;                    // K columns D..D+7 = (1, 0, ..., 0)
+  lc.vconst = C::ONES && (lc.c16 & 3) >= 2;       // V^T rows D.. = ones at D, zeros below
+  lc.vconst_off = C::CONSTB + ((lc.c16 & 3) == 3 ? 8 : 0);
+  lc.krow_off = c32 * C::ROWB + 16 * lc.h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vsel_const[e] = pack_h2(1.0f, 1.0f);
-  }
-  // Per-lane LDS byte offsets of the operand reads.
-  const int krow_off = c32 * C::ROWB + 16 * h;
-  int vrow_off[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) vrow_off[r] = (vrow(g) + 16 * r + (c16 >> 2)) * C::ROWB + 8 * (c16 & 3);
+  for (int r = 0; r < 2; ++r) lc.vrow_off[r] = (vrow(lc.g) + 16 * r + (lc.c16 >> 2)) * C::ROWB + 8 * (lc.c16 & 3);
 
-  f4 oacc[C::NQB][2][C::NDT];
-  float mrun[C::NQB], lsum[C::NQB];
+  // Tiles in the key sequence and this wave's copy instructions per tile.
+  int ntiles = 0;
+  bool full = true;  // every tile holds BN real keys: no masking anywhere
+  for (int s = 0; s < p.nseg; ++s) {
+    ntiles += (int)((p.seg[s].len + C::BN - 1) / C::BN);
+    full &= (p.seg[s].len % C::BN) == 0;
+  }
+  Copier<C> cp;
+  cp.ni = 0;
+#pragma unroll
+  for (int j = 0; j < C::NI; ++j) {
+    const int u = wave + kWaves * j;
+    const int uu = u >= C::LI ? u - C::LI : u;
+    const int c = uu * 64 + lc.lane;
+    cp.row[j] = c / C::CPR;
+    cp.ch[j] = c - cp.row[j] * C::CPR;
+    cp.ni += (u < 2 * C::LI) ? 1 : 0;
+  }
+
+  // Segment / offset of a tile -> its count of real keys; step to the next tile.
+  auto tile_valid = [&](int s, int64_t off) -> int { return (int)min((int64_t)C::BN, p.seg[s].len - off); };
+  auto tile_next = [&](int& s, int64_t& off) {
+    off += C::BN;
+    if (off >= p.seg[s].len) {
+      s += 1;
+      off = 0;
+    }
+  };
 
   for (int attempt = 0;; ++attempt) {
     const bool exact_all = attempt > 0;
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
-      mrun[qb] = 0.f;
-      lsum[qb] = 0.f;
+      ws.mrun[qb] = 0.f;
+      ws.lsum[qb] = 0.f;
 #pragma unroll
       for (int grp = 0; grp < 2; ++grp)
 #pragma unroll
-        for (int t = 0; t < C::NDT; ++t) oacc[qb][grp][t] = (f4){0.f, 0.f, 0.f, 0.f};
-      if (C::ONES && h) qf[qb][C::KST - 1][0] = (_Float16)0.0f;  // offset column: none yet
+        for (int t = 0; t < C::NDT; ++t) ws.oacc[qb][grp][t] = (f4){0.f, 0.f, 0.f, 0.f};
+      if (C::ONES && lc.h) ws.qf[qb][C::KST - 1][0] = (_Float16)0.0f;  // offset column: none yet
     }
+
+    cp.s = 0;
+    cp.off = 0;
+    cp.issued = 0;
+    while (cp.issued < C::NBUF - 1 && cp.issued < ntiles) issue_tile<C>(p, smem, cp, f, hd, wave);
+
+    // ---- tile 0: exact ----
+    int cs = 0;  // segment / offset of the tile being consumed
+    int64_t coff = 0;
+    wait_vm(cp.ni * (cp.issued - 1));  // tile 0 has landed
+    __syncthreads();
+    if (cp.issued < ntiles) issue_tile<C>(p, smem, cp, f, hd, wave);  // ring slot NBUF-1 is still unused
+    tile_step<C, false>(smem, 0, tile_valid(cs, coff), true, ws, lc);
+    tile_next(cs, coff);
+
     bool fast = false;
-
-    int s = 0;
-    int64_t off = 0;
-    issue_tile<C>(p, smem, 0, 0, f, hd, wave, lane);
-    for (int it = 0;; ++it) {
-      char* cur = smem + (it & 1) * C::BUFB;
-      const int valid = (int)min((int64_t)C::BN, p.seg[s].len - off);
-      int s_n = s;
-      int64_t off_n = off + C::BN;
-      if (off_n >= p.seg[s].len) {
-        s_n = s + 1;
-        off_n = 0;
-      }
-      const bool has_next = s_n < p.nseg;
-
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (has_next) issue_tile<C>(p, smem + ((it + 1) & 1) * C::BUFB, s_n, off_n, f, hd, wave, lane);
-
-      if (fast)
-        tile_step<C, true>(cur, qf, oacc, mrun, lsum, false, valid, lane, h, c16, g, kones, vsel_const, vsel_data,
-                           krow_off, vrow_off);
-      else
-        tile_step<C, false>(cur, qf, oacc, mrun, lsum, it == 0, valid, lane, h, c16, g, kones, vsel_const,
-                            vsel_data, krow_off, vrow_off);
-
-      if (it == 0 && !exact_all) {
-        // freeze the offset: from now on no tile maximum is taken
-        bool ok = true;
-        if (C::ONES) {
+    if (!exact_all) {
+      bool ok = true;
+      if (C::ONES) {
 #pragma unroll
-          for (int qb = 0; qb < C::NQB; ++qb) ok &= fabsf(mrun[qb]) <= kFastMaxOffset;
-          ok = __all(ok);
-          if (ok && h) {
+        for (int qb = 0; qb < C::NQB; ++qb) ok &= fabsf(ws.mrun[qb]) <= kFastMaxOffset;
+        ok = __all(ok);
+        if (ok && lc.h) {
 #pragma unroll
-            for (int qb = 0; qb < C::NQB; ++qb) qf[qb][C::KST - 1][0] = (_Float16)(-mrun[qb]);
-          }
+          for (int qb = 0; qb < C::NQB; ++qb) ws.qf[qb][C::KST - 1][0] = (_Float16)(-ws.mrun[qb]);  // offset joins the product
         }
-        fast = ok;
       }
-      if (!has_next) break;
-      s = s_n;
-      off = off_n;
+      fast = ok;
+    }
+
+    if (C::PIPE && fast && full && ntiles > 1) {
+      // ---- fast full tiles 1..ntiles-1, software pipelined over 32-key blocks ----
+      static_assert(!C::PIPE || C::NKB == 2, "the pipeline is written for two 32-key blocks per tile");
+      static_assert(!C::PIPE || C::NBUF >= 3, "the pipeline holds two tiles while the next one is copied");
+      // prologue: S^T and P^T of tile 1's first block, S^T of its second
+      wait_vm(cp.ni * (cp.issued - 2));  // tile 1 has landed
+      __syncthreads();                   // ... everywhere; tile 0 is free
+      if (cp.issued < ntiles && cp.issued < 1 + C::NBUF) issue_tile<C>(p, smem, cp, f, hd, wave);
+      f16v sA[C::NQB], sB[C::NQB];
+      h8 pA[C::NQB][2], pB[C::NQB][2];
+      {
+        const int kt = (1 % C::NBUF) * C::BUFB;
+        float alpha[C::NQB];
+        bool resc;
+        qk_block<C>(smem, kt, ws, lc, sA);
+        softmax_block<C, false>(sA, ws, lc, 32, false, pA, alpha, resc);
+        qk_block<C>(smem, kt + 32 * C::ROWB, ws, lc, sB);
+      }
+      for (int t = 1; t < ntiles; ++t) {
+        const bool more = t + 1 < ntiles;
+        int ns = cs;
+        int64_t noff = coff;
+        tile_next(ns, noff);
+        const int kt = (t % C::NBUF) * C::BUFB;
+        const int kn = ((t + 1) % C::NBUF) * C::BUFB;
+        if (more) {
+          wait_vm(cp.ni * (cp.issued - (t + 2)));  // tile t+1 has landed
+          __syncthreads();                         // ... everywhere; tiles up to t-1 are free
+          // tiles t and t+1 stay in use during this trip: refill only the slot of t-1
+          if (cp.issued < ntiles && cp.issued < t + C::NBUF) issue_tile<C>(p, smem, cp, f, hd, wave);
+          // b = 2t: softmax(2t+1) [sB -> pB], PV(2t) [pA], S^T(2t+2) [-> sA]
+          pipe_iteration<C>(smem, kt + C::TILEB, kn, sB, sA, pA, pB, ws, lc);
+          // b = 2t+1: softmax(2t+2) [sA -> pA], PV(2t+1) [pB], S^T(2t+3) [-> sB]
+          pipe_iteration<C>(smem, kt + C::TILEB + 32 * C::ROWB, kn + 32 * C::ROWB, sA, sB, pB, pA, ws, lc);
+        } else {
+          // drain: softmax(2t+1), PV(2t), PV(2t+1)
+          float alpha[C::NQB];
+          bool resc;
+          h8 va[C::NDT];
+          load_vt<C>(smem, kt + C::TILEB, lc, va);
+          softmax_block<C, false>(sB, ws, lc, 32, false, pB, alpha, resc);
+          pv_block<C>(va, pA, ws);
+          load_vt<C>(smem, kt + C::TILEB + 32 * C::ROWB, lc, va);
+          pv_block<C>(va, pB, ws);
+        }
+        cs = ns;
+        coff = noff;
+      }
+    } else {
+      // ---- remaining tiles one after another (exact unless fast) ----
+      for (int t = 1; t < ntiles; ++t) {
+        wait_vm(cp.ni * (cp.issued - (t + 1)));  // tile t has landed
+        __syncthreads();                         // ... everywhere; tile t-1 is free
+        if (cp.issued < ntiles) issue_tile<C>(p, smem, cp, f, hd, wave);
+        const int kt = (t % C::NBUF) * C::BUFB;
+        if (fast)
+          tile_step<C, true>(smem, kt, tile_valid(cs, coff), false, ws, lc);
+        else
+          tile_step<C, false>(smem, kt, tile_valid(cs, coff), false, ws, lc);
+        tile_next(cs, coff);
+      }
     }
 
     if (exact_all) break;
@@ -434,20 +632,22 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
     for (int qb = 0; qb < C::NQB; ++qb) {
       if (C::ONES) {
         constexpr int tl = C::D / 16, gl = (C::D % 16) / 4, rl = C::D % 4;
-        if (g == gl) {
+        if (lc.g == gl) {
 #pragma unroll
-          for (int grp = 0; grp < 2; ++grp) bad |= !(fabsf(oacc[qb][grp][tl][rl]) <= 3.0e38f);
+          for (int grp = 0; grp < 2; ++grp) bad |= !(fabsf(ws.oacc[qb][grp][tl][rl]) <= 3.0e38f);
         }
       } else {
-        bad |= !(fabsf(lsum[qb]) <= 3.0e38f);
+        bad |= !(fabsf(ws.lsum[qb]) <= 3.0e38f);
       }
     }
     bad = __any(bad);
-    if (lane == 0) flags[wave] = bad ? 1 : 0;
+    __syncthreads();  // every wave is done with the ring before it may be refilled
+    if (lc.lane == 0) flags[wave] = bad ? 1 : 0;
     __syncthreads();
-    const bool any_bad = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
+    bool any_bad = false;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) any_bad |= flags[w] != 0;
     if (!any_bad) break;
-    __syncthreads();  // every wave has read the flags and left the tile buffers
   }
 
   // ---- normalise and write O (fp16, round to nearest even) ----
@@ -455,26 +655,26 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
 #pragma unroll
   for (int qb = 0; qb < C::NQB; ++qb) {
     float tot = 0.f;
-    if (!C::ONES) tot = lsum[qb] + __shfl_xor(lsum[qb], 32, 64);
+    if (!C::ONES) tot = ws.lsum[qb] + __shfl_xor(ws.lsum[qb], 32, 64);
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp) {
       float l;
       if (C::ONES) {
         constexpr int tl = C::D / 16, gl = (C::D % 16) / 4, rl = C::D % 4;
-        l = __shfl(oacc[qb][grp][tl][rl], 16 * gl + c16, 64);
+        l = __shfl(ws.oacc[qb][grp][tl][rl], 16 * gl + lc.c16, 64);
       } else {
-        l = __shfl(tot, 16 * grp + c16, 64);
+        l = __shfl(tot, 16 * grp + lc.c16, 64);
       }
       const float inv = 1.0f / l;
-      const int row = qrow0 + 32 * qb + 16 * grp + c16;
+      const int row = qrow0 + 32 * qb + 16 * grp + lc.c16;
       if (row < p.Lq) {
 #pragma unroll
         for (int t = 0; t < C::NDT; ++t) {
-          const int col = 16 * t + 4 * g;
+          const int col = 16 * t + 4 * lc.g;
           if (col < C::D) {
             h4 out;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) out[r] = (_Float16)(oacc[qb][grp][t][r] * inv);
+            for (int r = 0; r < 4; ++r) out[r] = (_Float16)(ws.oacc[qb][grp][t][r] * inv);
             *reinterpret_cast<h4*>(ob + (int64_t)row * p.o_ld + col) = out;
           }
         }
@@ -483,10 +683,12 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
   }
 }
 
-template <int D, int NQB, int NKB, int MINB>
+template <int D, int NQB, int NKB, int NBUF, int MINB, bool PIPE>
 hipError_t launch_cfg(const KParams& kp, hipStream_t stream) {
-  using C = Cfg<D, NQB, NKB, MINB>;
+  using C = Cfg<D, NQB, NKB, NBUF, MINB, PIPE>;
   KParams p = kp;
+  for (int i = 0; i < p.nseg; ++i)
+    if (p.seg[i].ld * 2 * C::BN > 0x7fffffffLL) return hipErrorInvalidValue;  // 32-bit copy offsets
   p.nqt = (p.Lq + C::QWG - 1) / C::QWG;
   const int64_t blocks = (int64_t)p.nqt * p.F * p.H;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
@@ -512,10 +714,10 @@ hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream) {
   p.c2 = a.scale * kLog2e;
   for (int i = 0; i < PL_MAX_SEGMENTS; ++i) p.seg[i] = a.seg[i];
   switch (a.d) {
-    case 32: return launch_cfg<32, 2, 2, 2>(p, stream);
-    case 40: return launch_cfg<40, 2, 2, 2>(p, stream);
-    case 80: return launch_cfg<80, 1, 2, 2>(p, stream);
-    case 160: return launch_cfg<160, 1, 1, 1>(p, stream);
+    case 32: return launch_cfg<32, 2, 2, 4, 2, true>(p, stream);
+    case 40: return launch_cfg<40, 2, 2, 4, 2, true>(p, stream);
+    case 80: return launch_cfg<80, 1, 2, 3, 2, false>(p, stream);
+    case 160: return launch_cfg<160, 1, 2, 2, 1, false>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
