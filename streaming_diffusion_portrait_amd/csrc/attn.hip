@@ -212,6 +212,65 @@ __device__ __forceinline__ void issue_tile(const KParams& p, char* smem, Copier<
   }
   cp.issued += 1;
 }
+
+// Copy side for key sequences made of full tiles only: the (frame, head)
+// base addresses live in scalar registers and each lane's byte offsets are
+// fixed per segment, so issuing a tile costs no vector arithmetic.
+template <class C>
+struct FastCopier {
+  const char* kp;          // next tile's K rows for this (frame, head)
+  const char* vp;          // ... and V rows
+  int64_t step;            // bytes from one tile to the next (BN rows)
+  int rem;                 // tiles left in the current segment
+  int s;                   // current segment
+  unsigned loff[C::NI];    // per lane: byte offset of each copy instruction within a tile
+};
+
+template <class C>
+__device__ __forceinline__ void fast_seek(const KParams& p, FastCopier<C>& fc, const Copier<C>& cp, int s, int64_t off,
+                                          int f, int h) {
+  fc.s = s;
+  if (s >= p.nseg) return;
+  const AttnSegment& sg = p.seg[s];
+  const int64_t base = (int64_t)f * sg.frame_stride + off * sg.ld + (int64_t)h * C::D;
+  fc.kp = reinterpret_cast<const char*>(sg.k + base);
+  fc.vp = reinterpret_cast<const char*>(sg.v + base);
+  fc.step = sg.ld * 2 * C::BN;
+  fc.rem = (int)((sg.len - off) / C::BN);
+  const unsigned ld2 = (unsigned)(sg.ld * 2);
+#pragma unroll
+  for (int j = 0; j < C::NI; ++j) fc.loff[j] = (unsigned)cp.row[j] * ld2 + (unsigned)cp.ch[j] * 16u;
+}
+
+template <class C>
+__device__ __forceinline__ void fast_issue(const KParams& p, char* smem, FastCopier<C>& fc, Copier<C>& cp, int f,
+                                           int h, int wave) {
+  const unsigned buf = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)smem +
+                       (unsigned)((cp.issued % C::NBUF) * C::BUFB);
+#pragma unroll
+  for (int j = 0; j < C::NI; ++j) {
+    const int u = wave + kWaves * j;  // wave-uniform
+    if (u < 2 * C::LI) {
+      const bool isv = u >= C::LI;
+      const int uu = isv ? u - C::LI : u;
+      const unsigned m0 = __builtin_amdgcn_readfirstlane(buf + (isv ? C::TILEB : 0) + uu * 1024);
+      const uint64_t b64 = (uint64_t)(uintptr_t)(isv ? fc.vp : fc.kp);
+      // (readfirstlane yields a signed int: widen through unsigned so the low
+      // word never sign-extends into the high one)
+      const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b64 >> 32));
+      const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b64);
+      const uint64_t sbase = (hi << 32) | lo;  // uniform by construction
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :
+                   : "s"(m0), "v"(fc.loff[j]), "s"(sbase)
+                   : "memory", "m0");
+    }
+  }
+  fc.kp += fc.step;
+  fc.vp += fc.step;
+  cp.issued += 1;
+  if (--fc.rem == 0) fast_seek<C>(p, fc, cp, fc.s + 1, 0, f, h);
+}
 #pragma clang diagnostic pop
 
 // Per-wave register state.
@@ -428,12 +487,15 @@ __device__ __forceinline__ void pipe_iteration(const char* smem, int vblk, int k
                                                h8 (&p_out)[C::NQB][2], WaveState<C>& ws, const LaneCtx& lc) {
   float alpha[C::NQB];
   bool resc;
+  // S^T(b+2) first: its products must be complete when the next iteration's
+  // softmax reads them; PV(b) and the softmax fill the rest of the iteration.
+  qk_block<C>(smem, kblk_next, ws, lc, s_out);
   h8 va[C::NDT];
   load_vt<C>(smem, vblk, lc, va);
   softmax_block<C, false>(s_in, ws, lc, 32, false, p_out, alpha, resc);
   pv_block<C>(va, p_in, ws);
-  qk_block<C>(smem, kblk_next, ws, lc, s_out);
   sched_iteration<C>();
+  __builtin_amdgcn_sched_barrier(0);  // iterations do not mix: each keeps its own interleave
 }
 
 template <class C>
@@ -566,9 +628,11 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
       static_assert(!C::PIPE || C::NKB == 2, "the pipeline is written for two 32-key blocks per tile");
       static_assert(!C::PIPE || C::NBUF >= 3, "the pipeline holds two tiles while the next one is copied");
       // prologue: S^T and P^T of tile 1's first block, S^T of its second
+      FastCopier<C> fc;
+      fast_seek<C>(p, fc, cp, cp.s, cp.off, f, hd);
       wait_vm(cp.ni * (cp.issued - 2));  // tile 1 has landed
       __syncthreads();                   // ... everywhere; tile 0 is free
-      if (cp.issued < ntiles && cp.issued < 1 + C::NBUF) issue_tile<C>(p, smem, cp, f, hd, wave);
+      if (cp.issued < ntiles && cp.issued < 1 + C::NBUF) fast_issue<C>(p, smem, fc, cp, f, hd, wave);
       f16v sA[C::NQB], sB[C::NQB];
       h8 pA[C::NQB][2], pB[C::NQB][2];
       {
@@ -579,18 +643,22 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
         softmax_block<C, false>(sA, ws, lc, 32, false, pA, alpha, resc);
         qk_block<C>(smem, kt + 32 * C::ROWB, ws, lc, sB);
       }
+      // steady state: the copies of the NBUF-3 tiles after t+1 may stay in
+      // flight (the count is the smallest any wave issues, so waves with more
+      // copies per tile wait a little longer than they must)
+      constexpr int kSteadyWait = (2 * C::LI / kWaves) * (C::NBUF - 3);
       for (int t = 1; t < ntiles; ++t) {
         const bool more = t + 1 < ntiles;
-        int ns = cs;
-        int64_t noff = coff;
-        tile_next(ns, noff);
         const int kt = (t % C::NBUF) * C::BUFB;
         const int kn = ((t + 1) % C::NBUF) * C::BUFB;
         if (more) {
-          wait_vm(cp.ni * (cp.issued - (t + 2)));  // tile t+1 has landed
-          __syncthreads();                         // ... everywhere; tiles up to t-1 are free
+          if (cp.issued >= t + C::NBUF - 1)
+            wait_vm(kSteadyWait);  // tile t+1 has landed
+          else
+            wait_vm(0);
+          __syncthreads();  // ... everywhere; tiles up to t-1 are free
           // tiles t and t+1 stay in use during this trip: refill only the slot of t-1
-          if (cp.issued < ntiles && cp.issued < t + C::NBUF) issue_tile<C>(p, smem, cp, f, hd, wave);
+          if (cp.issued < ntiles && cp.issued < t + C::NBUF) fast_issue<C>(p, smem, fc, cp, f, hd, wave);
           // b = 2t: softmax(2t+1) [sB -> pB], PV(2t) [pA], S^T(2t+2) [-> sA]
           pipe_iteration<C>(smem, kt + C::TILEB, kn, sB, sA, pA, pB, ws, lc);
           // b = 2t+1: softmax(2t+2) [sA -> pA], PV(2t+1) [pB], S^T(2t+3) [-> sB]
@@ -606,8 +674,6 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
           load_vt<C>(smem, kt + C::TILEB + 32 * C::ROWB, lc, va);
           pv_block<C>(va, pB, ws);
         }
-        cs = ns;
-        coff = noff;
       }
     } else {
       // ---- remaining tiles one after another (exact unless fast) ----
