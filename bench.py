@@ -238,12 +238,12 @@ def main():
             f"({100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s)")
 
     if args.copy_calib:
-        # a plain device copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB): the yardstick
-        # that scales the FETCH_SIZE / WRITE_SIZE counters into bytes
+        # a plain elementwise copy kernel over exactly 1 GiB (reads 1 GiB, writes 1 GiB):
+        # the yardstick that scales the FETCH_SIZE / WRITE_SIZE counters into bytes
         src = torch.empty(2**28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
