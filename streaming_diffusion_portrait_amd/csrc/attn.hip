@@ -11,10 +11,13 @@
 //   * one workgroup = 4 wavefronts = one (head, frame, query tile); each wave
 //     owns NQB blocks of 32 query rows (the K/V operands read from LDS serve
 //     all of them, which keeps LDS traffic per score low);
-//   * K and V tiles of BN = 32*NKB keys are copied HBM -> LDS by direct-to-LDS
-//     loads (global_load_lds_dwordx4), row-major exactly as they sit in HBM
-//     (2*d bytes per key), into a ring of NBUF buffers that runs up to NBUF-1
-//     tiles ahead of the tile being consumed; one barrier per tile;
+//   * K and V tiles of BN = 64 keys are copied HBM -> LDS by direct-to-LDS
+//     loads (global_load_lds_dwordx4) into a ring of NBUF buffers that runs
+//     up to NBUF-1 tiles ahead of the tile being consumed; one barrier per
+//     tile.  A staged tile is plane-major: plane c holds the 16-byte chunk c
+//     (dims 8c..8c+7) of all 64 keys, so one wave-wide copy fills one plane,
+//     every lane keeps a single byte offset (its key row) and the operand
+//     reads below hit consecutive LDS addresses;
 //   * workgroup ids are remapped so that each of the 8 XCDs (ids are dealt
 //     round-robin to them) works on a contiguous range of (head, frame, tile),
 //     i.e. mostly on one head, whose shared bank keys then stay in its L2.
@@ -27,16 +30,18 @@
 //   O^T = V^T P^T v_mfma_f32_16x16x32_f16: B = P^T is assembled from the S^T
 //                 registers of two query halves with v_permlane16_swap, so
 //                 probabilities never touch LDS; A = V^T is read from the
-//                 row-major V tile with ds_read_b64_tr_b16 (transposing read),
+//                 staged V tile with ds_read_b64_tr_b16 (transposing read),
 //                 two reads per operand.  The order in which the swapped P^T
 //                 lists the keys fixes which V rows each transposing read
 //                 fetches (vrow() below).
 //
 // Software pipeline (fast tiles, per wave, 32-key blocks b): iteration b
 // evaluates softmax(b+1) on the vector ALU, O^T += V^T(b) P^T(b) and
-// S^T(b+2) = K(b+2) Q^T on the matrix core -- three independent streams that
-// are interleaved instruction by instruction, so the exponentials and
-// conversions issue while the matrix products execute.
+// S^T(b+2) = K(b+2) Q^T on the matrix core, and reads the K operands of
+// block b+3 and V of block b from LDS -- independent streams that are
+// interleaved instruction by instruction, so the exponentials and
+// conversions issue while the matrix products execute and no product waits
+// for an LDS read issued in the same iteration except PV(b) for V(b).
 //
 // Softmax (fp32, log2 units).  Q is pre-scaled by scale*log2(e) and rounded
 // to fp16 once, so the matrix core yields s = scale*log2(e)*q.k directly.
@@ -87,6 +92,12 @@ constexpr int kSchedMfma = 0x008, kSchedValu = 0x002, kSchedDsRead = 0x100;
 // for e >= 4, with vrow(g) = 0, 8, 4, 12 for g = 0..3.
 __device__ __forceinline__ int vrow(int g) { return 8 * (g & 1) + 4 * (g >> 1); }
 
+// Bytes of padding after each 1 KB plane of a staged tile; it moves the two
+// planes one transposing read touches onto different LDS banks.
+#ifndef PL_PLANE_PAD
+#define PL_PLANE_PAD 64
+#endif
+
 template <int D_, int NQB_, int NKB_, int NBUF_, int MINB_, bool PIPE_>
 struct Cfg {
   static constexpr int D = D_;
@@ -100,18 +111,21 @@ struct Cfg {
   static constexpr int KST = (D + 15) / 16;   // 16-wide contraction steps of S^T
   static constexpr int NDT = (D + 15) / 16;   // 16-row tiles of O^T
   static constexpr bool ONES = (D % 16) != 0; // padding column D carries ones / -m
-  static constexpr int ROWB = 2 * D;          // bytes per staged key row
-  static constexpr int TILEB = BN * ROWB;     // bytes of one K (or V) tile
-  static constexpr int CPR = D / 8;           // 16-byte chunks per key row
-  static constexpr int LI = BN * CPR / 64;    // wave-wide 16-byte load instructions per tile (K or V)
+  static constexpr int CPR = D / 8;           // 16-byte chunks per key row (dims 8c..8c+7)
+  static constexpr int NPL = 2 * KST;         // planes per tile: the chunks, then the (1, 0, ..., 0) plane if any
+  static constexpr int PLB = 64 * 16 + PL_PLANE_PAD;  // bytes per plane (64 keys x 16 bytes + padding)
+  static constexpr int KBLK = 32 * 16;        // byte step of a 32-key block within a plane
+  static constexpr int TILEB = NPL * PLB;     // bytes of one K (or V) tile
+  static constexpr int LI = CPR;              // wave-wide 16-byte load instructions per tile (K or V): one per plane
   static constexpr int NI = (2 * LI + kWaves - 1) / kWaves;  // load instructions per wave per tile (max)
   static constexpr int BUFB = 2 * TILEB;      // K tile + V tile
-  static constexpr int CONSTB = NBUF * BUFB;  // 16-byte constant chunk (1, 0, ..., 0) in fp16
-  static constexpr int LDSB = CONSTB + 128;   // ring + constant + slack read past the last row
+  static constexpr int LDSB = NBUF * BUFB;
   static_assert(D % 8 == 0, "head dim must be a multiple of 8");
   static_assert(!ONES || D % 16 == 8, "the ones column must start the upper half of the last step");
-  static_assert((BN * CPR) % 64 == 0, "a tile must be whole wave-wide load instructions");
-  static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2 to 4 buffers");
+  static_assert(NPL - CPR == (ONES ? 1 : 0), "one constant plane exactly when d leaves a padding column");
+  static_assert(BN == 64, "one plane per load instruction: 64 keys of 16 bytes");
+  static_assert(PLB % 16 == 0, "planes hold 16-byte chunks");
+  static_assert(NBUF >= 2 && NBUF <= 6, "ring of 2 to 6 buffers");
   static_assert(NI * (NBUF - 1) <= 24, "vmcnt wait table range");
 };
 
@@ -157,52 +171,72 @@ __device__ __forceinline__ void wait_vm(int n) {
 }
 #undef PL_VMCNT_CASE
 
-// The copy side of the ring: which tile comes next and this wave's share of
-// each tile's copy instructions.
+// Wave-uniform copies of values the compiler cannot prove uniform (they live
+// in scalar registers from here on).  readfirstlane yields a signed int:
+// widen through unsigned so a low word never sign-extends into the high one.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)((uint64_t)x >> 32));
+  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(uint64_t)x);
+  return (int64_t)((hi << 32) | lo);
+}
+__device__ __forceinline__ const char* uniform_ptr(const char* x) {
+  return reinterpret_cast<const char*>(uniform64((int64_t)(uintptr_t)x));
+}
+
+// The copy side of the ring.  A staged tile is plane-major: plane c holds the
+// 16-byte chunk c (dims 8c..8c+7) of each of the 64 keys, so one wave-wide
+// direct-to-LDS load (lane i's 16 bytes land at M0 + 16*i) fills one plane,
+// lane i copying key i.  Copy instruction u of a tile (u < LI: K plane u,
+// else V plane u - LI) belongs to wave u % kWaves.
 template <class C>
 struct Copier {
-  int s;           // segment of the next tile to copy
-  int64_t off;     // its first key within the segment
-  int issued;      // tiles copied so far
-  int ni;          // copy instructions this wave issues per tile
-  int row[C::NI];  // per lane: key row (within the tile) and 16-byte chunk of each instruction
-  int ch[C::NI];
+  int s;        // segment of the next tile to copy
+  int64_t off;  // its first key within the segment
+  int issued;   // tiles copied so far
+  int ni;       // copy instructions this wave issues per tile
 };
 
-// Issue this wave's share of the direct-to-LDS copies of the next tile and
-// advance.  (M0 is named as clobbered by the asm below; nothing else in this
-// kernel keeps a value in it.)
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// One wave-wide direct-to-LDS copy: 16 bytes from gbase + voff (per lane)
+// to LDS address m0 + 16*lane.  Written as asm so the compiler does not
+// serialise the LDS reads of the other buffers behind it; completion is
+// awaited explicitly (vmcnt) before the barrier that publishes the tile.  The
+// instruction has no register result.  (M0 is named as clobbered; nothing
+// else in this kernel keeps a value in it.)
+__device__ __forceinline__ void lds_dma16(unsigned m0, unsigned voff, const char* gbase) {
+  const uint64_t sbase = (uint64_t)(uintptr_t)uniform_ptr(gbase);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ unsigned lds_addr(const char* x) {
+  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)x;
+}
+
+// Issue this wave's share of the copies of the next tile and advance.  A
+// ragged last tile of a segment repeats its last real key in the lanes beyond
+// it (those keys are masked in the softmax).
 template <class C>
-__device__ __forceinline__ void issue_tile(const KParams& p, char* smem, Copier<C>& cp, int f, int h, int wave) {
+__device__ __forceinline__ void issue_tile(const KParams& p, char* smem, Copier<C>& cp, int f, int h, int wave,
+                                           int lane) {
   const AttnSegment& sg = p.seg[cp.s];
-  const int64_t valid = sg.len - cp.off;  // >= 1
+  const int valid = (int)min((int64_t)C::BN, sg.len - cp.off);  // >= 1
   const int64_t base = (int64_t)f * sg.frame_stride + cp.off * sg.ld + (int64_t)h * C::D;
   const char* kbase = reinterpret_cast<const char*>(sg.k + base);
   const char* vbase = reinterpret_cast<const char*>(sg.v + base);
-  const int ld2 = (int)(sg.ld * 2);
-  char* buf = smem + (cp.issued % C::NBUF) * C::BUFB;
+  const unsigned voff = (unsigned)min(lane, valid - 1) * (unsigned)(sg.ld * 2);
+  const unsigned buf = lds_addr(smem) + (unsigned)((cp.issued % C::NBUF) * C::BUFB);
 #pragma unroll
   for (int j = 0; j < C::NI; ++j) {
     const int u = wave + kWaves * j;  // wave-uniform
     if (u < 2 * C::LI) {
       const bool isv = u >= C::LI;
-      const int uu = isv ? u - C::LI : u;
-      int row = cp.row[j];
-      if (row >= valid) row = (int)valid - 1;  // ragged tail: duplicate a valid row (masked later)
-      const char* src = (isv ? vbase : kbase) + (row * ld2 + cp.ch[j] * 16);
-      const char* dst = buf + (isv ? C::TILEB : 0) + uu * 1024;
-      // Lane i's 16 bytes land at M0 + 16*i.  Written as asm so the compiler
-      // does not serialise the LDS reads of the other buffers behind this
-      // copy; completion is awaited explicitly (vmcnt) before the barrier
-      // that publishes the tile.  The instruction has no register result.
-      const unsigned m0 = __builtin_amdgcn_readfirstlane(
-          (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)dst);
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                   :
-                   : "s"(m0), "v"(src)
-                   : "memory", "m0");
+      const int pl = isv ? u - C::LI : u;
+      lds_dma16(buf + (isv ? C::TILEB : 0) + pl * C::PLB, voff, (isv ? vbase : kbase) + 16 * pl);
     }
   }
   cp.off += C::BN;
@@ -214,64 +248,51 @@ __device__ __forceinline__ void issue_tile(const KParams& p, char* smem, Copier<
 }
 
 // Copy side for key sequences made of full tiles only: the (frame, head)
-// base addresses live in scalar registers and each lane's byte offsets are
-// fixed per segment, so issuing a tile costs no vector arithmetic.
+// base addresses live in scalar registers and each lane's byte offset (its
+// key row) is fixed per segment, so issuing a tile costs no vector arithmetic.
 template <class C>
 struct FastCopier {
-  const char* kp;          // next tile's K rows for this (frame, head)
-  const char* vp;          // ... and V rows
-  int64_t step;            // bytes from one tile to the next (BN rows)
-  int rem;                 // tiles left in the current segment
-  int s;                   // current segment
-  unsigned loff[C::NI];    // per lane: byte offset of each copy instruction within a tile
+  const char* kp;  // next tile's K rows for this (frame, head)
+  const char* vp;  // ... and V rows
+  int64_t step;    // bytes from one tile to the next (BN rows)
+  int rem;         // tiles left in the current segment
+  int s;           // current segment
+  unsigned voff;   // per lane: byte offset of its key row
 };
 
 template <class C>
-__device__ __forceinline__ void fast_seek(const KParams& p, FastCopier<C>& fc, const Copier<C>& cp, int s, int64_t off,
-                                          int f, int h) {
-  fc.s = s;
-  if (s >= p.nseg) return;
-  const AttnSegment& sg = p.seg[s];
+__device__ __forceinline__ void fast_seek(const KParams& p, FastCopier<C>& fc, int s, int64_t off, int f, int h,
+                                          int lane) {
+  fc.s = __builtin_amdgcn_readfirstlane(s);
+  if (fc.s >= p.nseg) return;
+  const AttnSegment& sg = p.seg[fc.s];
+  off = uniform64(off);
   const int64_t base = (int64_t)f * sg.frame_stride + off * sg.ld + (int64_t)h * C::D;
-  fc.kp = reinterpret_cast<const char*>(sg.k + base);
-  fc.vp = reinterpret_cast<const char*>(sg.v + base);
-  fc.step = sg.ld * 2 * C::BN;
-  fc.rem = (int)((sg.len - off) / C::BN);
-  const unsigned ld2 = (unsigned)(sg.ld * 2);
-#pragma unroll
-  for (int j = 0; j < C::NI; ++j) fc.loff[j] = (unsigned)cp.row[j] * ld2 + (unsigned)cp.ch[j] * 16u;
+  fc.kp = uniform_ptr(reinterpret_cast<const char*>(sg.k + base));
+  fc.vp = uniform_ptr(reinterpret_cast<const char*>(sg.v + base));
+  fc.step = uniform64(sg.ld * 2 * C::BN);
+  fc.rem = __builtin_amdgcn_readfirstlane((int)((sg.len - off) / C::BN));
+  fc.voff = (unsigned)lane * (unsigned)(sg.ld * 2);
 }
 
 template <class C>
 __device__ __forceinline__ void fast_issue(const KParams& p, char* smem, FastCopier<C>& fc, Copier<C>& cp, int f,
-                                           int h, int wave) {
-  const unsigned buf = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)smem +
-                       (unsigned)((cp.issued % C::NBUF) * C::BUFB);
+                                           int h, int wave, int lane) {
+  const unsigned buf = lds_addr(smem) + (unsigned)((cp.issued % C::NBUF) * C::BUFB);
 #pragma unroll
   for (int j = 0; j < C::NI; ++j) {
     const int u = wave + kWaves * j;  // wave-uniform
     if (u < 2 * C::LI) {
       const bool isv = u >= C::LI;
-      const int uu = isv ? u - C::LI : u;
-      const unsigned m0 = __builtin_amdgcn_readfirstlane(buf + (isv ? C::TILEB : 0) + uu * 1024);
-      const uint64_t b64 = (uint64_t)(uintptr_t)(isv ? fc.vp : fc.kp);
-      // (readfirstlane yields a signed int: widen through unsigned so the low
-      // word never sign-extends into the high one)
-      const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b64 >> 32));
-      const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b64);
-      const uint64_t sbase = (hi << 32) | lo;  // uniform by construction
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :
-                   : "s"(m0), "v"(fc.loff[j]), "s"(sbase)
-                   : "memory", "m0");
+      const int pl = isv ? u - C::LI : u;
+      lds_dma16(buf + (isv ? C::TILEB : 0) + pl * C::PLB, fc.voff, (isv ? fc.vp : fc.kp) + 16 * pl);
     }
   }
   fc.kp += fc.step;
   fc.vp += fc.step;
   cp.issued += 1;
-  if (--fc.rem == 0) fast_seek<C>(p, fc, cp, fc.s + 1, 0, f, h);
+  if (--fc.rem == 0) fast_seek<C>(p, fc, fc.s + 1, 0, f, h, lane);
 }
-#pragma clang diagnostic pop
 
 // Per-wave register state.
 template <class C>
@@ -285,31 +306,41 @@ struct WaveState {
 // Lane constants.
 struct LaneCtx {
   int lane, h, c16, g;
-  int krow_off;      // K operand LDS byte offset within a 32-key block
-  int vrow_off[2];   // V^T operand LDS byte offsets of the two transposing reads
-  bool kconst;       // this lane's last K step is the constant (ones column) chunk
-  bool vconst;       // this lane's last V^T reads are constant chunks (rows >= D)
-  int vconst_off;    // ... at this LDS byte address
+  int krow_off;     // K operand LDS byte offset within a 32-key block (plane 0)
+  int vrow_off[2];  // V^T operand LDS byte offsets of the two transposing reads (planes 0, 1)
 };
+
+// K operands of one 32-key block: step st reads planes 2st (lanes 0..31)
+// and 2st+1 (lanes 32..63); the padding column D, if any, lies in the
+// constant plane.
+template <class C>
+__device__ __forceinline__ void load_k(const char* smem, int kblk, const LaneCtx& lc, h8 (&ka)[C::KST]) {
+#pragma unroll
+  for (int st = 0; st < C::KST; ++st)
+    ka[st] = *reinterpret_cast<const h8*>(smem + kblk + lc.krow_off + 2 * st * C::PLB);
+}
+
+// S^T = K Q^T for every query block of the wave, from K operands in registers.
+// (Steps outermost: consecutive products accumulate into different query
+// blocks, so none waits for the one just issued.)
+template <class C>
+__device__ __forceinline__ void qk_regs(const h8 (&ka)[C::KST], const WaveState<C>& ws, f16v (&sacc)[C::NQB]) {
+#pragma unroll
+  for (int qb = 0; qb < C::NQB; ++qb) sacc[qb] = (f16v){};
+#pragma unroll
+  for (int st = 0; st < C::KST; ++st)
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb)
+      sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[st], ws.qf[qb][st], sacc[qb], 0, 0, 0);
+}
 
 // S^T(block) = K(block) Q^T for every query block of the wave.
 template <class C>
 __device__ __forceinline__ void qk_block(const char* smem, int kblk, const WaveState<C>& ws, const LaneCtx& lc,
                                          f16v (&sacc)[C::NQB]) {
   h8 ka[C::KST];
-#pragma unroll
-  for (int st = 0; st < C::KST; ++st) {
-    int a = kblk + lc.krow_off + 32 * st;
-    if (C::ONES && st == C::KST - 1) a = lc.kconst ? C::CONSTB : a;
-    ka[st] = *reinterpret_cast<const h8*>(smem + a);
-  }
-#pragma unroll
-  for (int qb = 0; qb < C::NQB; ++qb) {
-    f16v acc = {};
-#pragma unroll
-    for (int st = 0; st < C::KST; ++st) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[st], ws.qf[qb][st], acc, 0, 0, 0);
-    sacc[qb] = acc;
-  }
+  load_k<C>(smem, kblk, lc, ka);
+  qk_regs<C>(ka, ws, sacc);
 }
 
 // V^T operands of one 32-key block.
@@ -317,12 +348,8 @@ template <class C>
 __device__ __forceinline__ void load_vt(const char* smem, int vblk, const LaneCtx& lc, h8 (&va)[C::NDT]) {
 #pragma unroll
   for (int t = 0; t < C::NDT; ++t) {
-    int a0 = vblk + 32 * t + lc.vrow_off[0];
-    int a1 = vblk + 32 * t + lc.vrow_off[1];
-    if (C::ONES && t == C::NDT - 1) {
-      a0 = lc.vconst ? lc.vconst_off : a0;
-      a1 = lc.vconst ? lc.vconst_off : a1;
-    }
+    const int a0 = vblk + 2 * t * C::PLB + lc.vrow_off[0];
+    const int a1 = vblk + 2 * t * C::PLB + lc.vrow_off[1];
     const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(smem + a0));
     const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(smem + a1));
     u4 w;
@@ -452,9 +479,9 @@ __device__ __forceinline__ void tile_step(const char* smem, int kt, int valid, b
 #pragma unroll
   for (int kb = 0; kb < C::NKB; ++kb) {
     f16v s[C::NQB];
-    qk_block<C>(smem, kt + kb * 32 * C::ROWB, ws, lc, s);
+    qk_block<C>(smem, kt + kb * C::KBLK, ws, lc, s);
     h8 va[C::NDT];
-    load_vt<C>(smem, kt + C::TILEB + kb * 32 * C::ROWB, lc, va);
+    load_vt<C>(smem, kt + C::TILEB + kb * C::KBLK, lc, va);
     h8 pb[C::NQB][2];
     float alpha[C::NQB];
     bool resc;
@@ -466,35 +493,51 @@ __device__ __forceinline__ void tile_step(const char* smem, int kt, int valid, b
 
 // Interleave hint for one pipelined iteration: LDS operand reads first, then
 // the softmax's vector work threaded between the matrix products.
+#ifndef PL_SCHED_PER
+#define PL_SCHED_PER 3
+#endif
 template <class C>
 __device__ __forceinline__ void sched_iteration() {
-  constexpr int nds = C::KST + 2 * C::NDT;
-  constexpr int nmfma = C::NQB * (C::KST + 2 * C::NDT);
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, nds, 0);
-  __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 0);
+  // V^T reads first (used last); the S^T products (operands already in
+  // registers) threaded with the softmax's vector work; then the reads of the
+  // next K operands (into the registers those products just read) and the PV
+  // products with the rest of the vector work
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * C::NDT, 0);
 #pragma unroll
-  for (int i = 0; i < nmfma; ++i) {
+  for (int i = 0; i < C::NQB * C::KST; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, PL_SCHED_PER, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::KST, 0);
+#pragma unroll
+  for (int i = 0; i < C::NQB * 2 * C::NDT; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, PL_SCHED_PER, 0);
   }
 }
 
-// One pipelined iteration over full blocks: softmax(b+1) [s_in -> p_out],
-// O^T += V^T(b) P^T(b) [p_in], S^T(b+2) [-> s_out].
-template <class C>
-__device__ __forceinline__ void pipe_iteration(const char* smem, int vblk, int kblk_next, f16v (&s_in)[C::NQB],
+// One pipelined iteration over full blocks (block b of the pipeline):
+//   S^T(b+2) = K(b+2) Q^T from K operands already in registers (ka_cur),
+//   K operands of block b+3 read from LDS into ka_next,
+//   softmax(b+1) [s_in -> p_out], O^T += V^T(b) P^T(b) [p_in].
+// The products need no LDS data of this iteration, the softmax needs scores
+// computed an iteration ago, and V^T(b) is read first and used last, so no
+// stream waits on another.  QK / SM / KR: which of the first three parts
+// exist (the pipeline's last iterations run past the end of the sequence).
+template <class C, bool QK, bool SM, bool KR>
+__device__ __forceinline__ void pipe_iteration(const char* smem, int vblk, int kblk3, f16v (&s_in)[C::NQB],
                                                f16v (&s_out)[C::NQB], const h8 (&p_in)[C::NQB][2],
-                                               h8 (&p_out)[C::NQB][2], WaveState<C>& ws, const LaneCtx& lc) {
+                                               h8 (&p_out)[C::NQB][2], const h8 (&ka_cur)[C::KST],
+                                               h8 (&ka_next)[C::KST], WaveState<C>& ws, const LaneCtx& lc) {
   float alpha[C::NQB];
   bool resc;
-  // S^T(b+2) first: its products must be complete when the next iteration's
-  // softmax reads them; PV(b) and the softmax fill the rest of the iteration.
-  qk_block<C>(smem, kblk_next, ws, lc, s_out);
   h8 va[C::NDT];
   load_vt<C>(smem, vblk, lc, va);
-  softmax_block<C, false>(s_in, ws, lc, 32, false, p_out, alpha, resc);
+  if (QK) qk_regs<C>(ka_cur, ws, s_out);
+  if (SM) softmax_block<C, false>(s_in, ws, lc, 32, false, p_out, alpha, resc);
+  if (KR) load_k<C>(smem, kblk3, lc, ka_next);  // after the products read ka_cur
   pv_block<C>(va, p_in, ws);
-  sched_iteration<C>();
+  if (QK && SM && KR) sched_iteration<C>();
   __builtin_amdgcn_sched_barrier(0);  // iterations do not mix: each keeps its own interleave
 }
 
@@ -543,14 +586,24 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
     }
   }
 
-  // The constant chunk (1, 0, ..., 0) used for the padding column D.
-  if (tid < 8) reinterpret_cast<_Float16*>(smem + C::CONSTB)[tid] = (_Float16)(tid == 0 ? 1.0f : 0.0f);
-  lc.kconst = C::ONES && lc.h;                    // K columns D..D+7 = (1, 0, ..., 0)
-  lc.vconst = C::ONES && (lc.c16 & 3) >= 2;       // V^T rows D.. = ones at D, zeros below
-  lc.vconst_off = C::CONSTB + ((lc.c16 & 3) == 3 ? 8 : 0);
-  lc.krow_off = c32 * C::ROWB + 16 * lc.h;
+  // The constant plane of every K and V tile (d = 40): chunk (1, 0, ..., 0)
+  // for every key -- K's column D is ones (it meets the offset column of Q),
+  // V^T's row D is ones (its products are the row sums).  The copies never
+  // write this plane; the first barrier below publishes it.
+  if (C::ONES) {
+    for (int i = tid >> 6; i < 2 * C::NBUF; i += kWaves) {
+      h8 one = {0, 0, 0, 0, 0, 0, 0, 0};
+      one[0] = (_Float16)1.0f;
+      *reinterpret_cast<h8*>(smem + i * C::TILEB + C::CPR * C::PLB + 16 * lc.lane) = one;
+    }
+  }
+  // K step st: lane half h reads plane 2st+h at key c32.  V^T read r of lane
+  // (g, c16): key vrow(g) + 16r + c16/4, dims 4(c16%4)..+3 of the 16-dim tile,
+  // i.e. plane 2t + (c16%4)/2, byte 8*(c16%2) of the key's chunk.
+  lc.krow_off = c32 * 16 + lc.h * C::PLB;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) lc.vrow_off[r] = (vrow(lc.g) + 16 * r + (lc.c16 >> 2)) * C::ROWB + 8 * (lc.c16 & 3);
+  for (int r = 0; r < 2; ++r)
+    lc.vrow_off[r] = (vrow(lc.g) + 16 * r + (lc.c16 >> 2)) * 16 + ((lc.c16 & 3) >> 1) * C::PLB + 8 * (lc.c16 & 1);
 
   // Tiles in the key sequence and this wave's copy instructions per tile.
   int ntiles = 0;
@@ -562,14 +615,7 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
   Copier<C> cp;
   cp.ni = 0;
 #pragma unroll
-  for (int j = 0; j < C::NI; ++j) {
-    const int u = wave + kWaves * j;
-    const int uu = u >= C::LI ? u - C::LI : u;
-    const int c = uu * 64 + lc.lane;
-    cp.row[j] = c / C::CPR;
-    cp.ch[j] = c - cp.row[j] * C::CPR;
-    cp.ni += (u < 2 * C::LI) ? 1 : 0;
-  }
+  for (int j = 0; j < C::NI; ++j) cp.ni += (wave + kWaves * j < 2 * C::LI) ? 1 : 0;
 
   // Segment / offset of a tile -> its count of real keys; step to the next tile.
   auto tile_valid = [&](int s, int64_t off) -> int { return (int)min((int64_t)C::BN, p.seg[s].len - off); };
@@ -597,14 +643,14 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
     cp.s = 0;
     cp.off = 0;
     cp.issued = 0;
-    while (cp.issued < C::NBUF - 1 && cp.issued < ntiles) issue_tile<C>(p, smem, cp, f, hd, wave);
+    while (cp.issued < C::NBUF - 1 && cp.issued < ntiles) issue_tile<C>(p, smem, cp, f, hd, wave, lc.lane);
 
     // ---- tile 0: exact ----
     int cs = 0;  // segment / offset of the tile being consumed
     int64_t coff = 0;
     wait_vm(cp.ni * (cp.issued - 1));  // tile 0 has landed
     __syncthreads();
-    if (cp.issued < ntiles) issue_tile<C>(p, smem, cp, f, hd, wave);  // ring slot NBUF-1 is still unused
+    if (cp.issued < ntiles) issue_tile<C>(p, smem, cp, f, hd, wave, lc.lane);  // ring slot NBUF-1 is still unused
     tile_step<C, false>(smem, 0, tile_valid(cs, coff), true, ws, lc);
     tile_next(cs, coff);
 
@@ -625,62 +671,64 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
 
     if (C::PIPE && fast && full && ntiles > 1) {
       // ---- fast full tiles 1..ntiles-1, software pipelined over 32-key blocks ----
+      // Pipeline block j (j = 0 .. nb-1) is half j%2 of tile 1 + j/2.  Iteration j
+      // reads V of block j and K of block j+3 from LDS, so before an odd
+      // iteration 2u+1 tile u+3 must have landed; tile u is then finished by
+      // every wave and its slot is refilled.
       static_assert(!C::PIPE || C::NKB == 2, "the pipeline is written for two 32-key blocks per tile");
-      static_assert(!C::PIPE || C::NBUF >= 3, "the pipeline holds two tiles while the next one is copied");
-      // prologue: S^T and P^T of tile 1's first block, S^T of its second
+      static_assert(!C::PIPE || C::NBUF >= 4, "the pipeline reads from three tiles while the next one is copied");
+      const int nb = 2 * (ntiles - 1);
+      auto kblk = [&](int j) { return ((1 + (j >> 1)) % C::NBUF) * C::BUFB + (j & 1) * C::KBLK; };
+      auto vblk = [&](int j) { return kblk(j) + C::TILEB; };
       FastCopier<C> fc;
-      fast_seek<C>(p, fc, cp, cp.s, cp.off, f, hd);
-      wait_vm(cp.ni * (cp.issued - 2));  // tile 1 has landed
-      __syncthreads();                   // ... everywhere; tile 0 is free
-      if (cp.issued < ntiles && cp.issued < 1 + C::NBUF) fast_issue<C>(p, smem, fc, cp, f, hd, wave);
+      fast_seek<C>(p, fc, cp.s, cp.off, f, hd, lc.lane);
+      // prologue: tiles 1 and 2 (if any) have landed; tile 0 is free
+      wait_vm(cp.ni * (cp.issued - min(3, ntiles)));
+      __syncthreads();
+      if (cp.issued < ntiles && cp.issued < 1 + C::NBUF) fast_issue<C>(p, smem, fc, cp, f, hd, wave, lc.lane);
       f16v sA[C::NQB], sB[C::NQB];
       h8 pA[C::NQB][2], pB[C::NQB][2];
+      h8 kaA[C::KST], kaB[C::KST];
       {
-        const int kt = (1 % C::NBUF) * C::BUFB;
         float alpha[C::NQB];
         bool resc;
-        qk_block<C>(smem, kt, ws, lc, sA);
+        qk_block<C>(smem, kblk(0), ws, lc, sA);
         softmax_block<C, false>(sA, ws, lc, 32, false, pA, alpha, resc);
-        qk_block<C>(smem, kt + 32 * C::ROWB, ws, lc, sB);
+        qk_block<C>(smem, kblk(1), ws, lc, sB);
+        if (2 < nb) load_k<C>(smem, kblk(2), lc, kaA);
       }
-      // steady state: the copies of the NBUF-3 tiles after t+1 may stay in
+      // steady state: the copies of the NBUF-4 tiles after u+3 may stay in
       // flight (the count is the smallest any wave issues, so waves with more
       // copies per tile wait a little longer than they must)
-      constexpr int kSteadyWait = (2 * C::LI / kWaves) * (C::NBUF - 3);
-      for (int t = 1; t < ntiles; ++t) {
-        const bool more = t + 1 < ntiles;
-        const int kt = (t % C::NBUF) * C::BUFB;
-        const int kn = ((t + 1) % C::NBUF) * C::BUFB;
-        if (more) {
-          if (cp.issued >= t + C::NBUF - 1)
-            wait_vm(kSteadyWait);  // tile t+1 has landed
-          else
-            wait_vm(0);
-          __syncthreads();  // ... everywhere; tiles up to t-1 are free
-          // tiles t and t+1 stay in use during this trip: refill only the slot of t-1
-          if (cp.issued < ntiles && cp.issued < t + C::NBUF) fast_issue<C>(p, smem, fc, cp, f, hd, wave);
-          // b = 2t: softmax(2t+1) [sB -> pB], PV(2t) [pA], S^T(2t+2) [-> sA]
-          pipe_iteration<C>(smem, kt + C::TILEB, kn, sB, sA, pA, pB, ws, lc);
-          // b = 2t+1: softmax(2t+2) [sA -> pA], PV(2t+1) [pB], S^T(2t+3) [-> sB]
-          pipe_iteration<C>(smem, kt + C::TILEB + 32 * C::ROWB, kn + 32 * C::ROWB, sA, sB, pB, pA, ws, lc);
-        } else {
-          // drain: softmax(2t+1), PV(2t), PV(2t+1)
-          float alpha[C::NQB];
-          bool resc;
-          h8 va[C::NDT];
-          load_vt<C>(smem, kt + C::TILEB, lc, va);
-          softmax_block<C, false>(sB, ws, lc, 32, false, pB, alpha, resc);
-          pv_block<C>(va, pA, ws);
-          load_vt<C>(smem, kt + C::TILEB + 32 * C::ROWB, lc, va);
-          pv_block<C>(va, pB, ws);
-        }
+      constexpr int kSteadyWait = (2 * C::LI / kWaves) * (C::NBUF - 4);
+      // Even blocks read (sB -> pB, sA <- S^T, pA into PV, K into kaB), odd
+      // blocks the mirror image, so no registers are copied.
+      int u = 0;
+      for (; 2 * u + 4 < nb; ++u) {
+        pipe_iteration<C, true, true, true>(smem, vblk(2 * u), kblk(2 * u + 3), sB, sA, pA, pB, kaA, kaB, ws, lc);
+        if (cp.issued >= u + C::NBUF)
+          wait_vm(kSteadyWait);  // tile u+3 has landed
+        else
+          wait_vm(0);
+        __syncthreads();  // ... everywhere; tile u is finished
+        if (cp.issued < ntiles && cp.issued < u + 1 + C::NBUF) fast_issue<C>(p, smem, fc, cp, f, hd, wave, lc.lane);
+        pipe_iteration<C, true, true, true>(smem, vblk(2 * u + 1), kblk(2 * u + 4), sA, sB, pB, pA, kaB, kaA, ws, lc);
       }
+      // Blocks 2u.. are left: four of them (every tile they need has landed
+      // and no copy remains), or two when the sequence has only two tiles.
+      if (nb - 2 * u == 4) {
+        pipe_iteration<C, true, true, true>(smem, vblk(2 * u), kblk(2 * u + 3), sB, sA, pA, pB, kaA, kaB, ws, lc);
+        pipe_iteration<C, true, true, false>(smem, vblk(2 * u + 1), 0, sA, sB, pB, pA, kaB, kaA, ws, lc);
+        u += 1;
+      }
+      pipe_iteration<C, false, true, false>(smem, vblk(2 * u), 0, sB, sA, pA, pB, kaA, kaB, ws, lc);
+      pipe_iteration<C, false, false, false>(smem, vblk(2 * u + 1), 0, sA, sB, pB, pA, kaB, kaA, ws, lc);
     } else {
       // ---- remaining tiles one after another (exact unless fast) ----
       for (int t = 1; t < ntiles; ++t) {
         wait_vm(cp.ni * (cp.issued - (t + 1)));  // tile t has landed
         __syncthreads();                         // ... everywhere; tile t-1 is free
-        if (cp.issued < ntiles) issue_tile<C>(p, smem, cp, f, hd, wave);
+        if (cp.issued < ntiles) issue_tile<C>(p, smem, cp, f, hd, wave, lc.lane);
         const int kt = (t % C::NBUF) * C::BUFB;
         if (fast)
           tile_step<C, true>(smem, kt, tile_valid(cs, coff), false, ws, lc);
@@ -710,10 +758,10 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
     __syncthreads();  // every wave is done with the ring before it may be refilled
     if (lc.lane == 0) flags[wave] = bad ? 1 : 0;
     __syncthreads();
-    bool any_bad = false;
+    int any_bad = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) any_bad |= flags[w] != 0;
-    if (!any_bad) break;
+    for (int w = 0; w < kWaves; ++w) any_bad |= flags[w];
+    if (!__builtin_amdgcn_readfirstlane(any_bad)) break;
   }
 
   // ---- normalise and write O (fp16, round to nearest even) ----
