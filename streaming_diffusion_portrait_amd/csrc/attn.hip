@@ -75,8 +75,6 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s4 lds_s4;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;      // log2 units a block max may exceed the running offset by
 constexpr float kFastMaxOffset = 1024.0f;  // |m| bound for freezing the offset in fp16
@@ -98,16 +96,18 @@ __device__ __forceinline__ int vrow(int g) { return 8 * (g & 1) + 4 * (g >> 1); 
 #define PL_PLANE_PAD 64
 #endif
 
-template <int D_, int NQB_, int NKB_, int NBUF_, int MINB_, bool PIPE_>
+template <int D_, int NQB_, int NKB_, int NBUF_, int MINB_, bool PIPE_, int W_>
 struct Cfg {
   static constexpr int D = D_;
+  static constexpr int W = W_;                // wavefronts per workgroup
+  static constexpr int THREADS = 64 * W;
   static constexpr int NQB = NQB_;            // 32-query blocks per wave
   static constexpr bool PIPE = PIPE_;         // software-pipelined fast tiles
   static constexpr int NKB = NKB_;            // 32-key blocks per tile
   static constexpr int NBUF = NBUF_;          // LDS tile buffers in the ring
   static constexpr int MINB = MINB_;          // workgroups per CU the register budget is sized for
   static constexpr int BN = 32 * NKB;         // keys per tile
-  static constexpr int QWG = 32 * NQB * kWaves;  // query rows per workgroup
+  static constexpr int QWG = 32 * NQB * W;     // query rows per workgroup
   static constexpr int KST = (D + 15) / 16;   // 16-wide contraction steps of S^T
   static constexpr int NDT = (D + 15) / 16;   // 16-row tiles of O^T
   static constexpr bool ONES = (D % 16) != 0; // padding column D carries ones / -m
@@ -117,7 +117,7 @@ struct Cfg {
   static constexpr int KBLK = 32 * 16;        // byte step of a 32-key block within a plane
   static constexpr int TILEB = NPL * PLB;     // bytes of one K (or V) tile
   static constexpr int LI = CPR;              // wave-wide 16-byte load instructions per tile (K or V): one per plane
-  static constexpr int NI = (2 * LI + kWaves - 1) / kWaves;  // load instructions per wave per tile (max)
+  static constexpr int NI = (2 * LI + W - 1) / W;  // load instructions per wave per tile (max)
   static constexpr int BUFB = 2 * TILEB;      // K tile + V tile
   static constexpr int LDSB = NBUF * BUFB;
   static_assert(D % 8 == 0, "head dim must be a multiple of 8");
@@ -187,7 +187,7 @@ __device__ __forceinline__ const char* uniform_ptr(const char* x) {
 // 16-byte chunk c (dims 8c..8c+7) of each of the 64 keys, so one wave-wide
 // direct-to-LDS load (lane i's 16 bytes land at M0 + 16*i) fills one plane,
 // lane i copying key i.  Copy instruction u of a tile (u < LI: K plane u,
-// else V plane u - LI) belongs to wave u % kWaves.
+// else V plane u - LI) belongs to wave u % W.
 template <class C>
 struct Copier {
   int s;        // segment of the next tile to copy
@@ -232,7 +232,7 @@ __device__ __forceinline__ void issue_tile(const KParams& p, char* smem, Copier<
   const unsigned buf = lds_addr(smem) + (unsigned)((cp.issued % C::NBUF) * C::BUFB);
 #pragma unroll
   for (int j = 0; j < C::NI; ++j) {
-    const int u = wave + kWaves * j;  // wave-uniform
+    const int u = wave + C::W * j;  // wave-uniform
     if (u < 2 * C::LI) {
       const bool isv = u >= C::LI;
       const int pl = isv ? u - C::LI : u;
@@ -281,7 +281,7 @@ __device__ __forceinline__ void fast_issue(const KParams& p, char* smem, FastCop
   const unsigned buf = lds_addr(smem) + (unsigned)((cp.issued % C::NBUF) * C::BUFB);
 #pragma unroll
   for (int j = 0; j < C::NI; ++j) {
-    const int u = wave + kWaves * j;  // wave-uniform
+    const int u = wave + C::W * j;  // wave-uniform
     if (u < 2 * C::LI) {
       const bool isv = u >= C::LI;
       const int pl = isv ? u - C::LI : u;
@@ -516,6 +516,95 @@ __device__ __forceinline__ void sched_iteration() {
   }
 }
 
+// The softmax of one fast block (offset already inside the scores) as a
+// stream of single vector instructions, so that a schedule can place each of
+// them: per query block, 16 exponentials, 8 packs to fp16 (each issued two
+// exponentials after its inputs, so it never waits for them) and 4 permlane16
+// swaps that assemble P^T.  kSmOps instructions per query block.
+constexpr int kSmOps = 28;
+template <class C>
+struct FastSoftmax {
+  f16v* s;          // [NQB] scores -> exponentials, in place
+  unsigned pk[C::NQB][8];
+  h8* pb;           // [NQB][2] P^T operands out
+  __device__ __forceinline__ void op(int v) {
+    const int qb = v / kSmOps, r = v % kSmOps;
+    if (r < 4) {  // exponentials 0..3
+      s[qb][r] = __builtin_amdgcn_exp2f(s[qb][r]);
+    } else if (r < 4 + 3 * 6) {  // (pack i, exponentials 2i+4, 2i+5) for i = 0..5
+      const int i = (r - 4) / 3, k = (r - 4) % 3;
+      if (k == 0) pk[qb][i] = pack_h2(s[qb][2 * i], s[qb][2 * i + 1]);
+      else s[qb][2 * i + 4 + (k - 1)] = __builtin_amdgcn_exp2f(s[qb][2 * i + 4 + (k - 1)]);
+    } else if (r < 24) {  // packs 6, 7
+      const int i = r - 16;
+      pk[qb][i] = pack_h2(s[qb][2 * i], s[qb][2 * i + 1]);
+    } else {  // swaps: pack (2j+x) with pack (2j+2+x) for j = 0, 2 and x = 0, 1
+      const int k = r - 24, x = k & 1, j = (k >> 1) * 4;
+      const auto sw = __builtin_amdgcn_permlane16_swap(pk[qb][j + x], pk[qb][j + 2 + x], false, false);
+      u4 b0 = __builtin_bit_cast(u4, pb[2 * qb]), b1 = __builtin_bit_cast(u4, pb[2 * qb + 1]);
+      b0[(k >> 1) * 2 + x] = sw[0];
+      b1[(k >> 1) * 2 + x] = sw[1];
+      pb[2 * qb] = __builtin_bit_cast(h8, b0);
+      pb[2 * qb + 1] = __builtin_bit_cast(h8, b1);
+    }
+  }
+};
+
+// Vector instructions placed after each S^T product and each PV product of a
+// steady pipelined iteration (the rest follow the last product).
+#ifndef PL_FIXED_ORDER
+#define PL_FIXED_ORDER 1
+#endif
+#ifndef PL_SLOT_QK
+#define PL_SLOT_QK 4
+#endif
+#ifndef PL_SLOT_PV
+#define PL_SLOT_PV 3
+#endif
+
+// Steady pipelined iteration with a fixed instruction order: the LDS reads,
+// then slots of one matrix product and a share of the softmax's vector
+// instructions, fenced so that the compiler keeps the interleave.  Computes
+// the same as pipe_iteration<C, true, true, true>.
+template <class C>
+__device__ __forceinline__ void pipe_iteration_fixed(const char* smem, int vblk, int kblk3, f16v (&s_in)[C::NQB],
+                                                     f16v (&s_out)[C::NQB], const h8 (&p_in)[C::NQB][2],
+                                                     h8 (&p_out)[C::NQB][2], const h8 (&ka_cur)[C::KST],
+                                                     h8 (&ka_next)[C::KST], WaveState<C>& ws, const LaneCtx& lc) {
+  static_assert(C::ONES, "the fast softmax stream needs the offset inside the scores");
+  constexpr int NQK = C::KST * C::NQB, NPV = C::NDT * C::NQB * 2, NM = NQK + NPV;
+  constexpr int NV = kSmOps * C::NQB;
+  h8 va[C::NDT];
+  load_vt<C>(smem, vblk, lc, va);
+  load_k<C>(smem, kblk3, lc, ka_next);
+  __builtin_amdgcn_sched_barrier(0);
+  FastSoftmax<C> sm;
+  sm.s = s_in;
+  sm.pb = &p_out[0][0];
+  int v = 0;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    if (m < NQK) {  // S^T(b+2): steps outermost, query blocks alternate
+      const int st = m / C::NQB, qb = m % C::NQB;
+      s_out[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka_cur[st], ws.qf[qb][st], st == 0 ? (f16v){} : s_out[qb],
+                                                          0, 0, 0);
+    } else {  // O^T += V^T(b) P^T(b): d tiles outermost (the V reads land in that order)
+      const int i = m - NQK, t = i / (2 * C::NQB), qb = (i / 2) % C::NQB, grp = i % 2;
+      ws.oacc[qb][grp][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t], p_in[qb][grp], ws.oacc[qb][grp][t], 0, 0, 0);
+    }
+    const int nv = m < NQK ? PL_SLOT_QK : PL_SLOT_PV;
+#pragma unroll
+    for (int k = 0; k < nv; ++k)
+      if (v + k < NV) sm.op(v + k);
+    v += nv;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+    if (k >= v) sm.op(k);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // One pipelined iteration over full blocks (block b of the pipeline):
 //   S^T(b+2) = K(b+2) Q^T from K operands already in registers (ka_cur),
 //   K operands of block b+3 read from LDS into ka_next,
@@ -541,10 +630,26 @@ __device__ __forceinline__ void pipe_iteration(const char* smem, int vblk, int k
   __builtin_amdgcn_sched_barrier(0);  // iterations do not mix: each keeps its own interleave
 }
 
+// A full pipelined iteration: the fixed-order form where the offset rides in
+// the scores (d = 40), else the compiler-scheduled one.
 template <class C>
-__global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams p) {
+__device__ __forceinline__ void pipe_steady(const char* smem, int vblk, int kblk3, f16v (&s_in)[C::NQB],
+                                            f16v (&s_out)[C::NQB], const h8 (&p_in)[C::NQB][2],
+                                            h8 (&p_out)[C::NQB][2], const h8 (&ka_cur)[C::KST], h8 (&ka_next)[C::KST],
+                                            WaveState<C>& ws, const LaneCtx& lc) {
+#if PL_FIXED_ORDER
+  if constexpr (C::ONES) {
+    pipe_iteration_fixed<C>(smem, vblk, kblk3, s_in, s_out, p_in, p_out, ka_cur, ka_next, ws, lc);
+    return;
+  }
+#endif
+  pipe_iteration<C, true, true, true>(smem, vblk, kblk3, s_in, s_out, p_in, p_out, ka_cur, ka_next, ws, lc);
+}
+
+template <class C>
+__global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDSB];
-  __shared__ int flags[kWaves];
+  __shared__ int flags[C::W];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -591,7 +696,7 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
   // V^T's row D is ones (its products are the row sums).  The copies never
   // write this plane; the first barrier below publishes it.
   if (C::ONES) {
-    for (int i = tid >> 6; i < 2 * C::NBUF; i += kWaves) {
+    for (int i = tid >> 6; i < 2 * C::NBUF; i += C::W) {
       h8 one = {0, 0, 0, 0, 0, 0, 0, 0};
       one[0] = (_Float16)1.0f;
       *reinterpret_cast<h8*>(smem + i * C::TILEB + C::CPR * C::PLB + 16 * lc.lane) = one;
@@ -615,7 +720,7 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
   Copier<C> cp;
   cp.ni = 0;
 #pragma unroll
-  for (int j = 0; j < C::NI; ++j) cp.ni += (wave + kWaves * j < 2 * C::LI) ? 1 : 0;
+  for (int j = 0; j < C::NI; ++j) cp.ni += (wave + C::W * j < 2 * C::LI) ? 1 : 0;
 
   // Segment / offset of a tile -> its count of real keys; step to the next tile.
   auto tile_valid = [&](int s, int64_t off) -> int { return (int)min((int64_t)C::BN, p.seg[s].len - off); };
@@ -700,24 +805,24 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
       // steady state: the copies of the NBUF-4 tiles after u+3 may stay in
       // flight (the count is the smallest any wave issues, so waves with more
       // copies per tile wait a little longer than they must)
-      constexpr int kSteadyWait = (2 * C::LI / kWaves) * (C::NBUF - 4);
+      constexpr int kSteadyWait = (2 * C::LI / C::W) * (C::NBUF - 4);
       // Even blocks read (sB -> pB, sA <- S^T, pA into PV, K into kaB), odd
       // blocks the mirror image, so no registers are copied.
       int u = 0;
       for (; 2 * u + 4 < nb; ++u) {
-        pipe_iteration<C, true, true, true>(smem, vblk(2 * u), kblk(2 * u + 3), sB, sA, pA, pB, kaA, kaB, ws, lc);
+        pipe_steady<C>(smem, vblk(2 * u), kblk(2 * u + 3), sB, sA, pA, pB, kaA, kaB, ws, lc);
         if (cp.issued >= u + C::NBUF)
           wait_vm(kSteadyWait);  // tile u+3 has landed
         else
           wait_vm(0);
         __syncthreads();  // ... everywhere; tile u is finished
         if (cp.issued < ntiles && cp.issued < u + 1 + C::NBUF) fast_issue<C>(p, smem, fc, cp, f, hd, wave, lc.lane);
-        pipe_iteration<C, true, true, true>(smem, vblk(2 * u + 1), kblk(2 * u + 4), sA, sB, pB, pA, kaB, kaA, ws, lc);
+        pipe_steady<C>(smem, vblk(2 * u + 1), kblk(2 * u + 4), sA, sB, pB, pA, kaB, kaA, ws, lc);
       }
       // Blocks 2u.. are left: four of them (every tile they need has landed
       // and no copy remains), or two when the sequence has only two tiles.
       if (nb - 2 * u == 4) {
-        pipe_iteration<C, true, true, true>(smem, vblk(2 * u), kblk(2 * u + 3), sB, sA, pA, pB, kaA, kaB, ws, lc);
+        pipe_steady<C>(smem, vblk(2 * u), kblk(2 * u + 3), sB, sA, pA, pB, kaA, kaB, ws, lc);
         pipe_iteration<C, true, true, false>(smem, vblk(2 * u + 1), 0, sA, sB, pB, pA, kaB, kaA, ws, lc);
         u += 1;
       }
@@ -760,7 +865,7 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
     __syncthreads();
     int any_bad = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) any_bad |= flags[w];
+    for (int w = 0; w < C::W; ++w) any_bad |= flags[w];
     if (!__builtin_amdgcn_readfirstlane(any_bad)) break;
   }
 
@@ -797,16 +902,16 @@ __global__ void __launch_bounds__(kThreads, C::MINB) refbank_attn_kernel(KParams
   }
 }
 
-template <int D, int NQB, int NKB, int NBUF, int MINB, bool PIPE>
+template <int D, int NQB, int NKB, int NBUF, int MINB, bool PIPE, int W>
 hipError_t launch_cfg(const KParams& kp, hipStream_t stream) {
-  using C = Cfg<D, NQB, NKB, NBUF, MINB, PIPE>;
+  using C = Cfg<D, NQB, NKB, NBUF, MINB, PIPE, W>;
   KParams p = kp;
   for (int i = 0; i < p.nseg; ++i)
     if (p.seg[i].ld * 2 * C::BN > 0x7fffffffLL) return hipErrorInvalidValue;  // 32-bit copy offsets
   p.nqt = (p.Lq + C::QWG - 1) / C::QWG;
   const int64_t blocks = (int64_t)p.nqt * p.F * p.H;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(refbank_attn_kernel<C>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(refbank_attn_kernel<C>, dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -828,10 +933,10 @@ hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream) {
   p.c2 = a.scale * kLog2e;
   for (int i = 0; i < PL_MAX_SEGMENTS; ++i) p.seg[i] = a.seg[i];
   switch (a.d) {
-    case 32: return launch_cfg<32, 2, 2, 4, 2, true>(p, stream);
-    case 40: return launch_cfg<40, 2, 2, 4, 2, true>(p, stream);
-    case 80: return launch_cfg<80, 1, 2, 3, 2, false>(p, stream);
-    case 160: return launch_cfg<160, 1, 2, 2, 1, false>(p, stream);
+    case 32: return launch_cfg<32, 2, 2, 4, 2, true, 4>(p, stream);
+    case 40: return launch_cfg<40, 2, 2, 4, 2, true, 4>(p, stream);
+    case 80: return launch_cfg<80, 1, 2, 3, 2, false, 4>(p, stream);
+    case 160: return launch_cfg<160, 1, 2, 2, 1, false, 4>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
