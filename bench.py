@@ -10,6 +10,7 @@ already resident in HBM; every launch goes through the C ABI (libpl.so).
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --layer d00 [--steps K] [--warmup W]    (one attention layer alone)
 
 The ``cpu_baseline`` leg times the fp64 CPU oracle on a bounded sample of the
 same workload (a few (frame, head) pairs of the first 64^2 layer); it is a
@@ -49,6 +50,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the DDIM bandwidth sweep")
     ap.add_argument("--copy-calib", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--layer", default=None,
+                    help="profiling mode: launch only this attention layer (d00, d10, m, ...) "
+                         "--warmup + --steps times and print its timing as the JSON line")
     return ap.parse_args()
 
 
@@ -86,6 +90,45 @@ def traffic_record(kernel_key):
     return None
 
 
+def one_layer(args, B, todev, m, F, H):
+    """Launch one attention layer of the round alone (for counter and trace runs)."""
+    import torch
+
+    names = [n for n, _, _ in inputs_layers()]
+    if args.layer not in names:
+        log(f"unknown layer {args.layer}; one of {' '.join(names)}")
+        sys.exit(2)
+    from streaming_diffusion_portrait_amd import inputs
+    li = names.index(args.layer)
+    _, L, C = inputs.SD15_LAYERS[li]
+    lay = inputs.attention_layer(1000 * SEED + li, F, L, C, m)
+    q = todev(lay["q"])
+    segs = [(todev(lay["k_self"]), todev(lay["v_self"]))]
+    segs += [(todev(k), todev(v)) for k, v in zip(lay["bank_k"], lay["bank_v"])]
+    out = torch.empty_like(q)
+    call = B.PreparedAttn(q, segs, H, out)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / max(args.steps, 1) * 1e3
+    fl = attention_flops(F, L, C, L * (2 + m))
+    tf = fl / (us * 1e-6) / 1e12
+    print(json.dumps({"layer": args.layer, "L": L, "C": C, "d": C // H, "m": m, "launches": args.steps,
+                      "us_per_launch": round(us, 2), "tflops": round(tf, 1),
+                      "pct_fp16_peak": round(100 * tf / PEAK_FP16_TFLOPS, 2)}), flush=True)
+
+
+def inputs_layers():
+    from streaming_diffusion_portrait_amd import inputs
+    return inputs.SD15_LAYERS
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -110,6 +153,9 @@ def main():
     m = inputs.round_m(SEED) if args.m is None else int(args.m)
     F, H = 16, 8
     todev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    if args.layer is not None:
+        one_layer(args, B, todev, m, F, H)
+        return
 
     # ---- inputs: fresh seeded tensors per layer -------------------------------------------------
     t0 = time.perf_counter()
