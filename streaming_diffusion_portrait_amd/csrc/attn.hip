@@ -62,6 +62,8 @@
 //     v_dot2_f32_f16 on the packed probabilities (other head dims).
 #include "pl_internal.h"
 
+#include <type_traits>
+
 namespace pl {
 namespace {
 
@@ -732,8 +734,14 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
     }
   };
 
-  for (int attempt = 0;; ++attempt) {
-    const bool exact_all = attempt > 0;
+  // One pass over the whole key sequence.  The first pass freezes the offset
+  // after tile 0 (fast tiles); if that overflowed anywhere in the workgroup, a
+  // second pass recomputes everything with exact maxima on every tile.  The
+  // two passes are separate instantiations (not one loop), so the rare exact
+  // pass does not share register assignments with the fast one.  Returns
+  // whether the pass must be redone.
+  auto pass = [&](auto exact_tag) -> bool {
+    constexpr bool exact_all = decltype(exact_tag)::value;
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
       ws.mrun[qb] = 0.f;
@@ -843,7 +851,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
       }
     }
 
-    if (exact_all) break;
+    if (exact_all) return false;
     // A frozen offset is only unsafe if some probability left the fp16 range:
     // then a row sum is inf or NaN.  Decide for the whole workgroup.
     bool bad = false;
@@ -866,8 +874,9 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
     int any_bad = 0;
 #pragma unroll
     for (int w = 0; w < C::W; ++w) any_bad |= flags[w];
-    if (!__builtin_amdgcn_readfirstlane(any_bad)) break;
-  }
+    return __builtin_amdgcn_readfirstlane(any_bad) != 0;
+  };
+  if (pass(std::false_type{})) pass(std::true_type{});
 
   // ---- normalise and write O (fp16, round to nearest even) ----
   _Float16* ob = p.o + (int64_t)f * p.o_fs + (int64_t)hd * C::D;
