@@ -19,12 +19,18 @@ juhe.plus, "PersonaLive" for short, and the hysenlabs repository review):
   (PersonaLive, section "抗身份漂移的补丁" / anti identity-drift patch).
 * ``pile``       -- the ``latents_pile`` queue state machine
   (PersonaLive, section "流式金字塔去噪").
+* ``noise``      -- the pile's device-side roll: counter-based window noise,
+  the staircase prefill and the first frames' motion interpolation
+  (PersonaLive, sections "流式金字塔去噪", "首帧怎么办" and the TensorRT
+  section's ``new_noise`` input and ``bind()``).
 
 Every floating-point computation here is float64.  Each function states the
 passage it follows; readings of points the pages leave open are listed in the
 repository's design notes.  Parity status: every function here is pinned by
 ``tests/test_oracle_*.py`` against brute force, closed forms, invariants or a
-library routine; none is "parity unpinned".
+library routine.  The staircase prefill's recipe (the reference latent noised
+to each level) is a reading of a passage that does not state it: the
+arithmetic is pinned, the choice of content is "parity unpinned".
 """
 
 from .attention import refbank_attention, attend_rows, concat_segments
@@ -36,6 +42,7 @@ from .ddim import (
 )
 from .motion import motion_bank_min_l2
 from .pile import PyramidPile
+from .noise import philox4x64, uniform24, window_noise, staircase_prefill, lerp_points
 
 __all__ = [
     "refbank_attention",
@@ -47,4 +54,9 @@ __all__ = [
     "pyramid_ddim_step",
     "motion_bank_min_l2",
     "PyramidPile",
+    "philox4x64",
+    "uniform24",
+    "window_noise",
+    "staircase_prefill",
+    "lerp_points",
 ]
