@@ -38,7 +38,7 @@ typedef int32_t pl_status;
 #define PL_EUNSUPPORTED 2  /* valid in principle but not implemented (head dim, alignment) */
 #define PL_EDEVICE 3       /* the HIP runtime reported an error at launch */
 
-#define PL_ABI_VERSION 1
+#define PL_ABI_VERSION 2
 #define PL_MAX_SEGMENTS 8       /* key segments per attention call: self + reference + anchors (5 used) */
 #define PL_MAX_WINDOWS 8        /* windows per pile (the pages use 4) */
 #define PL_MAX_MOTION_BANK 4    /* reference embedding + at most 3 anchors */
@@ -144,6 +144,65 @@ pl_status pl_pyramid_ddim_step(const float* x_t, const float* eps, float* x_prev
                                const int32_t* t_host, int32_t step_len,
                                const double* alphas_cumprod_host, int32_t T,
                                double final_alpha_cumprod, int32_t emit_window, void* stream);
+
+/* Same step, and the pile rolls on the device: when emit_window >= 0 the
+ * leaving window's slot of x_prev receives the next round's new window --
+ * pure N(0, 1) noise, pl_window_noise(seed, new_window_id) -- instead of its
+ * own x_prev, which the pile discards anyway (that window is popped after
+ * this step).  PersonaLive, section 流式金字塔去噪: each round a new window of
+ * noise enters at the top timestep; the TensorRT section's bind() keeps the
+ * rolling latents on the device between rounds, the new window arriving as
+ * the new_noise input.  Writing it here costs no extra memory traffic: those
+ * bytes are written by the step anyway.  With x_prev aliasing x_t the pile
+ * is ready for the next round (pl_pile_begin_round returns that slot as the
+ * new window's slot).  Other arguments and errors: as pl_pyramid_ddim_step. */
+pl_status pl_pyramid_ddim_step_roll(const float* x_t, const float* eps, float* x_prev, float* x0_out,
+                                    int32_t W, int64_t elems_per_window,
+                                    const int32_t* t_host, int32_t step_len,
+                                    const double* alphas_cumprod_host, int32_t T,
+                                    double final_alpha_cumprod, int32_t emit_window,
+                                    uint64_t seed, uint64_t new_window_id, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Window noise, staircase prefill, first-frames interpolation
+ *
+ * PersonaLive, section 流式金字塔去噪: windows of pure noise enter the pile;
+ * section 首帧怎么办: the queue starts with three windows (12 frames) of
+ * staircase noise, and the first frames' pose / expression inputs are 12 + 1
+ * linearly interpolated points from the reference's to the first driving
+ * frame's, the last point dropped.  The pages do not say how noise is drawn;
+ * here it is a pure function of (seed, window id, element):
+ *
+ *   Philox-4x64-10 (Salmon et al., "Parallel random numbers: as easy as 1,
+ *   2, 3", SC 2011) with key (seed, window id) and counter (i / 4, 0, 0, 0)
+ *   gives four 64-bit words for elements 4(i/4) .. 4(i/4)+3; word x maps to
+ *   u = ((x >> 40) + 1) / 2^24 in (0, 1]; words (0, 1) and (2, 3) give two
+ *   normals each, r cos(2 pi u_odd) and r sin(2 pi u_odd) with
+ *   r = sqrt(-2 ln u_even) (Box-Muller), computed in fp32.
+ * ------------------------------------------------------------------------ */
+
+/* out: device fp32 [n], n in 1..2^40, any alignment. */
+pl_status pl_window_noise(float* out, int64_t n, uint64_t seed, uint64_t window_id, void* stream);
+
+/* Staircase prefill: slot w of the pile (w < n_windows) holds the window at
+ * t = w * step_len: sqrt(a) * ref + sqrt(1 - a) * noise(seed, w), with
+ * a = alpha_bar[t] from the table (NULL: SD scaled_linear, T = 1000) and
+ * window ids 0 .. n_windows-1 (as pl_pile_init with prefill numbers them).
+ * Reading: the pages say "staircase noise" and the reference image; what
+ * exactly is noised is not stated -- here the reference latent.
+ *   ref   device fp32 [elems_per_window] (e.g. the reference frame's latent
+ *         tiled over the window's frames); must not overlap the pile.
+ *   pile  device fp32 [n_windows][elems_per_window].
+ *   n_windows in 1..PL_MAX_WINDOWS with (n_windows-1)*step_len < T. */
+pl_status pl_pile_prefill(const float* ref, float* pile, int32_t n_windows, int64_t elems_per_window,
+                          int32_t step_len, const double* alphas_cumprod_host, int32_t T, uint64_t seed,
+                          void* stream);
+
+/* out[k][i] = a[i] + (b[i] - a[i]) * k / n for k = 0 .. n-1 (n + 1 evenly
+ * spaced points from a to b, the last one, b, dropped), fp32.
+ *   a, b  device fp32 [D]; out device fp32 [n][D], not overlapping a or b.
+ *   D in 1..2^40, n in 1..65535 (12 on the pages). */
+pl_status pl_lerp_points(const float* a, const float* b, int64_t D, int32_t n, float* out, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * Motion-bank minimum-L2 drift check

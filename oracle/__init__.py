@@ -42,7 +42,7 @@ from .ddim import (
 )
 from .motion import motion_bank_min_l2
 from .pile import PyramidPile
-from .noise import philox4x64, uniform24, window_noise, staircase_prefill, lerp_points
+from .noise import philox4x64, uniform24, window_noise, noise_at, staircase_prefill, lerp_points
 
 __all__ = [
     "refbank_attention",
@@ -57,6 +57,7 @@ __all__ = [
     "philox4x64",
     "uniform24",
     "window_noise",
+    "noise_at",
     "staircase_prefill",
     "lerp_points",
 ]

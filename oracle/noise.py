@@ -73,19 +73,37 @@ def uniform24(word):
 def window_noise(seed, window_id, n):
     """N(0, 1) noise of one window: n values, fp64, by the recipe above."""
     out = np.empty(n, dtype=np.float64)
-    key = (seed, window_id)
     for blk in range((n + 3) // 4):
-        w = philox4x64((blk, 0, 0, 0), key)
-        u = [uniform24(x) for x in w]
-        z = []
-        for a, b in ((u[0], u[1]), (u[2], u[3])):
-            r = np.sqrt(-2.0 * np.log(a))
-            z += [r * np.cos(2.0 * np.pi * b), r * np.sin(2.0 * np.pi * b)]
+        z = window_noise_block(seed, window_id, blk)
         for j in range(4):
             i = 4 * blk + j
             if i < n:
                 out[i] = z[j]
     return out
+
+
+def noise_at(seed, window_id, indices):
+    """Elements ``indices`` of window_noise(seed, window_id, ...), fp64 (for sampled checks)."""
+    idx = np.asarray(indices, dtype=np.int64)
+    out = np.empty(idx.size, dtype=np.float64)
+    cache = {}
+    for j, i in enumerate(idx.tolist()):
+        blk = i // 4
+        if blk not in cache:
+            cache[blk] = window_noise_block(seed, window_id, blk)
+        out[j] = cache[blk][i % 4]
+    return out
+
+
+def window_noise_block(seed, window_id, blk):
+    """The four normals of elements 4*blk .. 4*blk+3 (the recipe in the module docstring)."""
+    w = philox4x64((blk, 0, 0, 0), (seed, window_id))
+    u = [uniform24(x) for x in w]
+    z = []
+    for a, b in ((u[0], u[1]), (u[2], u[3])):
+        r = np.sqrt(-2.0 * np.log(a))
+        z += [r * np.cos(2.0 * np.pi * b), r * np.sin(2.0 * np.pi * b)]
+    return z
 
 
 def staircase_prefill(ref, seed, n_windows, step_len=333, alphas_cumprod=None):

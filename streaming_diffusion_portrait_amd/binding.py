@@ -31,6 +31,10 @@ EXPORTED = (
     "pl_refbank_attn_workspace_size",
     "pl_refbank_attn",
     "pl_pyramid_ddim_step",
+    "pl_pyramid_ddim_step_roll",
+    "pl_window_noise",
+    "pl_pile_prefill",
+    "pl_lerp_points",
     "pl_motion_bank_min_l2",
     "pl_pile_init",
     "pl_pile_begin_round",
@@ -98,6 +102,16 @@ def load():
     lib.pl_pyramid_ddim_step.restype = i32
     lib.pl_pyramid_ddim_step.argtypes = [vp, vp, vp, vp, i32, i64, ctypes.POINTER(i32), i32,
                                          ctypes.POINTER(f64), i32, f64, i32, vp]
+    u64 = ctypes.c_uint64
+    lib.pl_pyramid_ddim_step_roll.restype = i32
+    lib.pl_pyramid_ddim_step_roll.argtypes = [vp, vp, vp, vp, i32, i64, ctypes.POINTER(i32), i32,
+                                              ctypes.POINTER(f64), i32, f64, i32, u64, u64, vp]
+    lib.pl_window_noise.restype = i32
+    lib.pl_window_noise.argtypes = [vp, i64, u64, u64, vp]
+    lib.pl_pile_prefill.restype = i32
+    lib.pl_pile_prefill.argtypes = [vp, vp, i32, i64, i32, ctypes.POINTER(f64), i32, u64, vp]
+    lib.pl_lerp_points.restype = i32
+    lib.pl_lerp_points.argtypes = [vp, vp, i64, i32, vp, vp]
     lib.pl_motion_bank_min_l2.restype = i32
     lib.pl_motion_bank_min_l2.argtypes = [vp, i32, vp, i32, i32, f32, vp, vp, vp, vp]
     lib.pl_pile_init.restype = i32
@@ -135,6 +149,22 @@ def pl_refbank_attn_workspace_size(*args):
 
 def pl_pyramid_ddim_step(*args):
     return load().pl_pyramid_ddim_step(*args)
+
+
+def pl_pyramid_ddim_step_roll(*args):
+    return load().pl_pyramid_ddim_step_roll(*args)
+
+
+def pl_window_noise(*args):
+    return load().pl_window_noise(*args)
+
+
+def pl_pile_prefill(*args):
+    return load().pl_pile_prefill(*args)
+
+
+def pl_lerp_points(*args):
+    return load().pl_lerp_points(*args)
 
 
 def pl_motion_bank_min_l2(*args):
@@ -233,13 +263,22 @@ def refbank_attn(q, segments, heads, out=None, scale=None, stream=None):
     return out
 
 
+def _schedule(alphas_cumprod):
+    if alphas_cumprod is None:
+        return None, 1000
+    ab = (ctypes.c_double * len(alphas_cumprod))(*[float(a) for a in alphas_cumprod])
+    return ab, len(alphas_cumprod)
+
+
 def pyramid_ddim_step(x_t, eps, t_windows, x_prev=None, x0_out=None, emit_window=-1, step_len=333,
-                      alphas_cumprod=None, final_alpha_cumprod=-1.0, stream=None):
+                      alphas_cumprod=None, final_alpha_cumprod=-1.0, stream=None, roll=None):
     """Per-window DDIM step over a window-major fp32 pile (see ``pl_pyramid_ddim_step``).
 
     ``x_t``/``eps``: fp32 device tensors whose leading axis splits into
     ``W = len(t_windows)`` contiguous windows.  ``x_prev`` may be ``x_t``
-    (in place).  Returns ``(x_prev, x0_out)``.
+    (in place).  ``roll=(seed, new_window_id)`` calls
+    ``pl_pyramid_ddim_step_roll``: the emitted window's slot of ``x_prev``
+    then holds the next window's noise.  Returns ``(x_prev, x0_out)``.
     """
     _need(x_t, torch.float32, "x_t")
     _need(eps, torch.float32, "eps")
@@ -261,18 +300,66 @@ def pyramid_ddim_step(x_t, eps, t_windows, x_prev=None, x0_out=None, emit_window
         if not x0_out.is_contiguous() or x0_out.numel() != per:
             raise ValueError("x0_out must be contiguous with one window's size")
     ts = (ctypes.c_int32 * W)(*[int(t) for t in t_windows])
-    if alphas_cumprod is None:
-        ab_ptr, T = None, 1000
+    ab_ptr, T = _schedule(alphas_cumprod)
+    args = [ctypes.c_void_p(x_t.data_ptr()), ctypes.c_void_p(eps.data_ptr()), ctypes.c_void_p(x_prev.data_ptr()),
+            ctypes.c_void_p(x0_out.data_ptr()) if x0_out is not None else None,
+            W, per, ts, int(step_len), ab_ptr, T, float(final_alpha_cumprod), int(emit_window)]
+    if roll is None:
+        _check("pl_pyramid_ddim_step", pl_pyramid_ddim_step(*args, _stream_ptr(stream)))
     else:
-        ab = (ctypes.c_double * len(alphas_cumprod))(*[float(a) for a in alphas_cumprod])
-        ab_ptr, T = ab, len(alphas_cumprod)
-    st = pl_pyramid_ddim_step(ctypes.c_void_p(x_t.data_ptr()), ctypes.c_void_p(eps.data_ptr()),
-                              ctypes.c_void_p(x_prev.data_ptr()),
-                              ctypes.c_void_p(x0_out.data_ptr()) if x0_out is not None else None,
-                              W, per, ts, int(step_len), ab_ptr, T, float(final_alpha_cumprod), int(emit_window),
-                              _stream_ptr(stream))
-    _check("pl_pyramid_ddim_step", st)
+        seed, new_id = roll
+        _check("pl_pyramid_ddim_step_roll",
+               pl_pyramid_ddim_step_roll(*args, int(seed), int(new_id), _stream_ptr(stream)))
     return x_prev, x0_out
+
+
+def window_noise(n_or_out, seed, window_id, stream=None):
+    """N(0, 1) noise of one window (see ``pl_window_noise``): fp32 device [n]."""
+    if isinstance(n_or_out, torch.Tensor):
+        out = n_or_out
+        _need(out, torch.float32, "out")
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+    else:
+        out = torch.empty(int(n_or_out), dtype=torch.float32, device="cuda")
+    _check("pl_window_noise", pl_window_noise(ctypes.c_void_p(out.data_ptr()), out.numel(), int(seed),
+                                              int(window_id), _stream_ptr(stream)))
+    return out
+
+
+def pile_prefill(ref, n_windows, seed, step_len=333, alphas_cumprod=None, out=None, stream=None):
+    """Staircase prefill (see ``pl_pile_prefill``): fp32 [n_windows, ref.numel()]."""
+    _need(ref, torch.float32, "ref")
+    if not ref.is_contiguous():
+        raise ValueError("ref must be contiguous")
+    per = ref.numel()
+    if out is None:
+        out = torch.empty((n_windows, per), dtype=torch.float32, device=ref.device)
+    _need(out, torch.float32, "out")
+    if not out.is_contiguous() or out.numel() < n_windows * per:
+        raise ValueError("out must be contiguous with n_windows windows")
+    ab_ptr, T = _schedule(alphas_cumprod)
+    _check("pl_pile_prefill", pl_pile_prefill(ctypes.c_void_p(ref.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                              int(n_windows), per, int(step_len), ab_ptr, T, int(seed),
+                                              _stream_ptr(stream)))
+    return out
+
+
+def lerp_points(a, b, n, out=None, stream=None):
+    """n evenly spaced points from a towards b, b excluded (see ``pl_lerp_points``): fp32 [n, D]."""
+    _need(a, torch.float32, "a")
+    _need(b, torch.float32, "b")
+    if not (a.is_contiguous() and b.is_contiguous()) or a.numel() != b.numel():
+        raise ValueError("a and b must be contiguous with equal sizes")
+    D = a.numel()
+    if out is None:
+        out = torch.empty((int(n), D), dtype=torch.float32, device=a.device)
+    _need(out, torch.float32, "out")
+    if not out.is_contiguous() or out.numel() != int(n) * D:
+        raise ValueError("out must be contiguous [n, D]")
+    _check("pl_lerp_points", pl_lerp_points(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), D,
+                                            int(n), ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream)))
+    return out
 
 
 def motion_bank_min_l2(query, bank, threshold=17.0, out=None, stream=None):

@@ -12,6 +12,7 @@
 // emitted element).  The grid is 2-D: blockIdx.y selects the window, so the
 // coefficients are wave-uniform (scalar registers) and no per-element
 // division is needed.  Loads and stores are 16 B per lane.
+#include "philox.h"
 #include "pl_internal.h"
 
 namespace pl {
@@ -48,8 +49,15 @@ ddim_vec4_kernel(const f4v* x_t, const f4v* eps, f4v* x_prev,
       const int64_t i = base + (int64_t)u * kDdimThreads;
       if (i < n4_per_window) {
         f4v pv;
+        if (emit && cf.roll) {
+          // the leaving window's slot becomes next round's new window: its own
+          // x_prev is never used, so the slot takes the new window's noise
+          // (float4 i of the window is noise block i)
+          pv = normal4(cf.seed, cf.new_id, (uint64_t)i);
+        } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) pv[k] = fmaf(a, xv[u][k], b * ev[u][k]);
+          for (int k = 0; k < 4; ++k) pv[k] = fmaf(a, xv[u][k], b * ev[u][k]);
+        }
         __builtin_nontemporal_store(pv, pw + i);
         if (emit) {
           f4v z;
@@ -73,8 +81,11 @@ ddim_scalar_kernel(const float* x_t, const float* eps, float* x_prev,
   for (int64_t i = (int64_t)blockIdx.x * kDdimThreads + threadIdx.x; i < n_per_window;
        i += (int64_t)gridDim.x * kDdimThreads) {
     const float xv = x_t[off + i], ev = eps[off + i];
-    x_prev[off + i] = fmaf(a, xv, b * ev);
     if (emit) x0_out[i] = fmaf(c, xv, d * ev);
+    if (emit && cf.roll)
+      x_prev[off + i] = normal4(cf.seed, cf.new_id, (uint64_t)(i >> 2))[i & 3];
+    else
+      x_prev[off + i] = fmaf(a, xv, b * ev);
   }
 }
 

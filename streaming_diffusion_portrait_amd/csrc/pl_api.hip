@@ -55,6 +55,73 @@ const SdSchedule& sd_schedule() {
 
 }  // namespace
 
+namespace {
+
+// The resolved noise schedule of a call (user table or the built-in one).
+pl_status resolve_schedule(const char* fn, const double* alphas_cumprod_host, int32_t T, const double** ab) {
+  if (alphas_cumprod_host) {
+    if (T < 1) return fail(PL_EINVAL, "%s: T must be >= 1", fn);
+    for (int i = 0; i < T; ++i)
+      if (!(alphas_cumprod_host[i] > 0.0 && alphas_cumprod_host[i] <= 1.0))
+        return fail(PL_EINVAL, "%s: alphas_cumprod[%d] not in (0, 1]", fn, i);
+    *ab = alphas_cumprod_host;
+  } else {
+    if (T != 1000) return fail(PL_EINVAL, "%s: the built-in schedule has T = 1000 (got %d)", fn, T);
+    *ab = sd_schedule().ab;
+  }
+  return PL_OK;
+}
+
+pl_status ddim_step_impl(const float* x_t, const float* eps, float* x_prev, float* x0_out, int32_t W,
+                         int64_t elems_per_window, const int32_t* t_host, int32_t step_len,
+                         const double* alphas_cumprod_host, int32_t T, double final_alpha_cumprod,
+                         int32_t emit_window, int32_t roll, uint64_t seed, uint64_t new_id, void* stream) {
+  if (!x_t || !eps || !x_prev) return fail(PL_EINVAL, "pl_pyramid_ddim_step: x_t, eps, x_prev must be non-null");
+  if (!t_host) return fail(PL_EINVAL, "pl_pyramid_ddim_step: t_host must be non-null");
+  if (W < 1 || W > PL_MAX_WINDOWS)
+    return fail(PL_EINVAL, "pl_pyramid_ddim_step: W must be in [1, %d] (got %d)", PL_MAX_WINDOWS, W);
+  if (elems_per_window < 1) return fail(PL_EINVAL, "pl_pyramid_ddim_step: elems_per_window must be >= 1");
+  if (elems_per_window > (int64_t(1) << 40)) return fail(PL_EINVAL, "pl_pyramid_ddim_step: elems_per_window too large");
+  if (step_len < 1) return fail(PL_EINVAL, "pl_pyramid_ddim_step: step_len must be >= 1");
+  if (emit_window < -1 || emit_window >= W)
+    return fail(PL_EINVAL, "pl_pyramid_ddim_step: emit_window must be -1 or in [0, W) (got %d)", emit_window);
+  if (emit_window >= 0 && !x0_out) return fail(PL_EINVAL, "pl_pyramid_ddim_step: x0_out is required when emitting");
+  const double* ab = nullptr;
+  if (pl_status st = resolve_schedule("pl_pyramid_ddim_step", alphas_cumprod_host, T, &ab)) return st;
+  double fin = final_alpha_cumprod;
+  if (fin < 0.0) fin = ab[0];
+  if (!(fin > 0.0 && fin <= 1.0)) return fail(PL_EINVAL, "pl_pyramid_ddim_step: final_alpha_cumprod not in (0, 1]");
+  pl::DdimLaunch a;
+  std::memset(&a, 0, sizeof(a));
+  for (int w = 0; w < W; ++w) {
+    const int t = t_host[w];
+    if (t < 0 || t >= T) return fail(PL_EINVAL, "pl_pyramid_ddim_step: t[%d] = %d not in [0, %d)", w, t, T);
+    const double at = ab[t];
+    const int prev = t - step_len;
+    const double ap = prev >= 0 ? ab[prev] : fin;
+    // x0 = (x_t - sqrt(1-at) eps)/sqrt(at); x_prev = sqrt(ap) x0 + sqrt(1-ap) eps
+    const double c = 1.0 / std::sqrt(at);
+    const double d = -std::sqrt(1.0 - at) / std::sqrt(at);
+    a.a[w] = (float)(std::sqrt(ap) * c);
+    a.b[w] = (float)(std::sqrt(ap) * d + std::sqrt(1.0 - ap));
+    a.c[w] = (float)c;
+    a.d[w] = (float)d;
+  }
+  a.x_t = x_t;
+  a.eps = eps;
+  a.x_prev = x_prev;
+  a.x0_out = emit_window >= 0 ? x0_out : nullptr;
+  a.W = W;
+  a.elems_per_window = elems_per_window;
+  a.emit_window = emit_window;
+  a.roll = roll;
+  a.seed = seed;
+  a.new_id = new_id;
+  return device_status(pl::launch_pyramid_ddim(a, static_cast<hipStream_t>(stream)), "pl_pyramid_ddim_step launch");
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t pl_abi_version(void) { return PL_ABI_VERSION; }
@@ -142,54 +209,84 @@ pl_status pl_pyramid_ddim_step(const float* x_t, const float* eps, float* x_prev
                                int64_t elems_per_window, const int32_t* t_host, int32_t step_len,
                                const double* alphas_cumprod_host, int32_t T, double final_alpha_cumprod,
                                int32_t emit_window, void* stream) {
-  if (!x_t || !eps || !x_prev) return fail(PL_EINVAL, "pl_pyramid_ddim_step: x_t, eps, x_prev must be non-null");
-  if (!t_host) return fail(PL_EINVAL, "pl_pyramid_ddim_step: t_host must be non-null");
-  if (W < 1 || W > PL_MAX_WINDOWS)
-    return fail(PL_EINVAL, "pl_pyramid_ddim_step: W must be in [1, %d] (got %d)", PL_MAX_WINDOWS, W);
-  if (elems_per_window < 1) return fail(PL_EINVAL, "pl_pyramid_ddim_step: elems_per_window must be >= 1");
-  if (elems_per_window > (int64_t(1) << 40)) return fail(PL_EINVAL, "pl_pyramid_ddim_step: elems_per_window too large");
-  if (step_len < 1) return fail(PL_EINVAL, "pl_pyramid_ddim_step: step_len must be >= 1");
-  if (emit_window < -1 || emit_window >= W)
-    return fail(PL_EINVAL, "pl_pyramid_ddim_step: emit_window must be -1 or in [0, W) (got %d)", emit_window);
-  if (emit_window >= 0 && !x0_out) return fail(PL_EINVAL, "pl_pyramid_ddim_step: x0_out is required when emitting");
-  const double* ab;
-  if (alphas_cumprod_host) {
-    if (T < 1) return fail(PL_EINVAL, "pl_pyramid_ddim_step: T must be >= 1");
-    ab = alphas_cumprod_host;
-    for (int i = 0; i < T; ++i)
-      if (!(ab[i] > 0.0 && ab[i] <= 1.0))
-        return fail(PL_EINVAL, "pl_pyramid_ddim_step: alphas_cumprod[%d] not in (0, 1]", i);
-  } else {
-    if (T != 1000) return fail(PL_EINVAL, "pl_pyramid_ddim_step: the built-in schedule has T = 1000 (got %d)", T);
-    ab = sd_schedule().ab;
-  }
-  double fin = final_alpha_cumprod;
-  if (fin < 0.0) fin = ab[0];
-  if (!(fin > 0.0 && fin <= 1.0)) return fail(PL_EINVAL, "pl_pyramid_ddim_step: final_alpha_cumprod not in (0, 1]");
-  pl::DdimLaunch a;
+  return ddim_step_impl(x_t, eps, x_prev, x0_out, W, elems_per_window, t_host, step_len, alphas_cumprod_host, T,
+                        final_alpha_cumprod, emit_window, 0, 0, 0, stream);
+}
+
+pl_status pl_pyramid_ddim_step_roll(const float* x_t, const float* eps, float* x_prev, float* x0_out, int32_t W,
+                                    int64_t elems_per_window, const int32_t* t_host, int32_t step_len,
+                                    const double* alphas_cumprod_host, int32_t T, double final_alpha_cumprod,
+                                    int32_t emit_window, uint64_t seed, uint64_t new_window_id, void* stream) {
+  return ddim_step_impl(x_t, eps, x_prev, x0_out, W, elems_per_window, t_host, step_len, alphas_cumprod_host, T,
+                        final_alpha_cumprod, emit_window, 1, seed, new_window_id, stream);
+}
+
+// ---------------------------------------------------------------------------
+pl_status pl_window_noise(float* out, int64_t n, uint64_t seed, uint64_t window_id, void* stream) {
+  if (!out) return fail(PL_EINVAL, "pl_window_noise: out must be non-null");
+  if (n < 1 || n > (int64_t(1) << 40)) return fail(PL_EINVAL, "pl_window_noise: n must be in [1, 2^40]");
+  pl::NoiseLaunch a;
   std::memset(&a, 0, sizeof(a));
-  for (int w = 0; w < W; ++w) {
-    const int t = t_host[w];
-    if (t < 0 || t >= T) return fail(PL_EINVAL, "pl_pyramid_ddim_step: t[%d] = %d not in [0, %d)", w, t, T);
-    const double at = ab[t];
-    const int prev = t - step_len;
-    const double ap = prev >= 0 ? ab[prev] : fin;
-    // x0 = (x_t - sqrt(1-at) eps)/sqrt(at); x_prev = sqrt(ap) x0 + sqrt(1-ap) eps
-    const double c = 1.0 / std::sqrt(at);
-    const double d = -std::sqrt(1.0 - at) / std::sqrt(at);
-    a.a[w] = (float)(std::sqrt(ap) * c);
-    a.b[w] = (float)(std::sqrt(ap) * d + std::sqrt(1.0 - ap));
-    a.c[w] = (float)c;
-    a.d[w] = (float)d;
+  a.ref = nullptr;
+  a.out = out;
+  a.n = n;
+  a.out_stride = n;
+  a.nw = 1;
+  a.seed = seed;
+  a.id0 = window_id;
+  a.ca[0] = 0.f;
+  a.cb[0] = 1.f;
+  return device_status(pl::launch_noise_affine(a, static_cast<hipStream_t>(stream)), "pl_window_noise launch");
+}
+
+pl_status pl_pile_prefill(const float* ref, float* pile, int32_t n_windows, int64_t elems_per_window,
+                          int32_t step_len, const double* alphas_cumprod_host, int32_t T, uint64_t seed,
+                          void* stream) {
+  if (!ref || !pile) return fail(PL_EINVAL, "pl_pile_prefill: ref and pile must be non-null");
+  if (n_windows < 1 || n_windows > PL_MAX_WINDOWS)
+    return fail(PL_EINVAL, "pl_pile_prefill: n_windows must be in [1, %d] (got %d)", PL_MAX_WINDOWS, n_windows);
+  if (elems_per_window < 1 || elems_per_window > (int64_t(1) << 40))
+    return fail(PL_EINVAL, "pl_pile_prefill: elems_per_window must be in [1, 2^40]");
+  if (step_len < 1) return fail(PL_EINVAL, "pl_pile_prefill: step_len must be >= 1");
+  const double* ab = nullptr;
+  if (pl_status st = resolve_schedule("pl_pile_prefill", alphas_cumprod_host, T, &ab)) return st;
+  if ((int64_t)(n_windows - 1) * step_len >= T)
+    return fail(PL_EINVAL, "pl_pile_prefill: window %d would sit at t = %lld >= T", n_windows - 1,
+                (long long)(n_windows - 1) * step_len);
+  const int64_t bytes = elems_per_window * (int64_t)sizeof(float);
+  const char* r0 = reinterpret_cast<const char*>(ref);
+  const char* p0 = reinterpret_cast<const char*>(pile);
+  if (r0 < p0 + bytes * n_windows && p0 < r0 + bytes)
+    return fail(PL_EINVAL, "pl_pile_prefill: ref must not overlap the pile");
+  pl::NoiseLaunch a;
+  std::memset(&a, 0, sizeof(a));
+  a.ref = ref;
+  a.out = pile;
+  a.n = elems_per_window;
+  a.out_stride = elems_per_window;
+  a.nw = n_windows;
+  a.seed = seed;
+  a.id0 = 0;
+  for (int w = 0; w < n_windows; ++w) {
+    const double at = ab[w * step_len];
+    a.ca[w] = (float)std::sqrt(at);
+    a.cb[w] = (float)std::sqrt(1.0 - at);
   }
-  a.x_t = x_t;
-  a.eps = eps;
-  a.x_prev = x_prev;
-  a.x0_out = emit_window >= 0 ? x0_out : nullptr;
-  a.W = W;
-  a.elems_per_window = elems_per_window;
-  a.emit_window = emit_window;
-  return device_status(pl::launch_pyramid_ddim(a, static_cast<hipStream_t>(stream)), "pl_pyramid_ddim_step launch");
+  return device_status(pl::launch_noise_affine(a, static_cast<hipStream_t>(stream)), "pl_pile_prefill launch");
+}
+
+pl_status pl_lerp_points(const float* a, const float* b, int64_t D, int32_t n, float* out, void* stream) {
+  if (!a || !b || !out) return fail(PL_EINVAL, "pl_lerp_points: pointers must be non-null");
+  if (D < 1 || D > (int64_t(1) << 40)) return fail(PL_EINVAL, "pl_lerp_points: D must be in [1, 2^40]");
+  if (n < 1 || n > 65535) return fail(PL_EINVAL, "pl_lerp_points: n must be in [1, 65535] (got %d)", n);
+  const int64_t bytes = D * (int64_t)sizeof(float);
+  const char* o0 = reinterpret_cast<const char*>(out);
+  for (const float* src : {a, b}) {
+    const char* s0 = reinterpret_cast<const char*>(src);
+    if (s0 < o0 + bytes * n && o0 < s0 + bytes) return fail(PL_EINVAL, "pl_lerp_points: out must not overlap a or b");
+  }
+  return device_status(pl::launch_lerp_points(a, b, D, n, out, static_cast<hipStream_t>(stream)),
+                       "pl_lerp_points launch");
 }
 
 // ---------------------------------------------------------------------------

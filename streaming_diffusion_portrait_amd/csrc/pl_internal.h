@@ -43,9 +43,25 @@ struct DdimLaunch {
   int32_t emit_window;  // -1 = none
   // per-window coefficients: x_prev = a*x_t + b*eps, x0 = c*x_t + d*eps
   float a[PL_MAX_WINDOWS], b[PL_MAX_WINDOWS], c[PL_MAX_WINDOWS], d[PL_MAX_WINDOWS];
+  // roll: the emitted window's x_prev slot receives noise(seed, new_id)
+  int32_t roll;
+  uint64_t seed, new_id;
 };
 
 hipError_t launch_pyramid_ddim(const DdimLaunch& a, hipStream_t stream);
+
+// ---- pile roll: window noise, staircase prefill, interpolation -----------------
+struct NoiseLaunch {
+  const float* ref;    // nullptr: pure noise
+  float* out;          // nw windows of n elements, out_stride apart
+  int64_t n, out_stride;
+  int32_t nw;
+  uint64_t seed, id0;  // window w draws noise(seed, id0 + w)
+  float ca[PL_MAX_WINDOWS], cb[PL_MAX_WINDOWS];
+};
+
+hipError_t launch_noise_affine(const NoiseLaunch& a, hipStream_t stream);
+hipError_t launch_lerp_points(const float* a, const float* b, int64_t D, int n, float* out, hipStream_t stream);
 
 // ---- motion-bank min-L2 -------------------------------------------------------
 struct MotionLaunch {

@@ -9,6 +9,10 @@ import numpy as np
 ATTN_MAX_ABS = 1e-2
 ATTN_MEAN_ABS = 1e-3
 DDIM_REL = 1e-5
+# Window noise in fp32: u is exact; ln u, the square root and sin/cos(2 pi u)
+# are each within a few ulp, so |z - z_fp64| <= ~2e-6 for |z| <= 5.8 (the
+# largest normal a 24-bit uniform can give); the bound leaves a 5x margin.
+NOISE_ABS = 1e-5
 
 
 def say(*msg):

@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pl_abi_version() == 1
+    assert lib.pl_abi_version() == 2
     assert [B.status_name(s) for s in range(4)] == ["PL_OK", "PL_EINVAL", "PL_EUNSUPPORTED", "PL_EDEVICE"]
     assert B.status_name(99) == "PL_UNKNOWN"
 
@@ -125,6 +125,38 @@ def test_ddim_rejects_bad_schedule(lib):
     ab = (ctypes.c_double * 3)(0.9, 0.0, 0.5)
     assert _ddim(t=(2, 1, 0, 0), ab=ab, T=3) == B.PL_EINVAL
     assert "alphas_cumprod[1]" in B.last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(x=None), dict(W=0), dict(emit=4), dict(x0=None), dict(T=999)])
+def test_ddim_roll_rejects(lib, kw):
+    args = dict(x=A, e=A2, xp=A, x0=A2, W=4, n=65536, t=(999, 666, 333, 0), step=333, ab=None, T=1000,
+                fin=-1.0, emit=3)
+    args.update(kw)
+    ts = (ctypes.c_int32 * 4)(*args["t"])
+    st = B.pl_pyramid_ddim_step_roll(args["x"], args["e"], args["xp"], args["x0"], args["W"], args["n"], ts,
+                                     args["step"], args["ab"], args["T"], args["fin"], args["emit"], 7, 11, None)
+    assert st == B.PL_EINVAL
+    assert B.last_error() != ""
+
+
+def test_noise_prefill_lerp_reject(lib):
+    assert B.pl_window_noise(None, 16, 1, 2, None) == B.PL_EINVAL
+    assert B.pl_window_noise(A, 0, 1, 2, None) == B.PL_EINVAL
+    # prefill: null pointers, window count, the top window beyond the schedule, overlap
+    assert B.pl_pile_prefill(None, A, 3, 64, 333, None, 1000, 5, None) == B.PL_EINVAL
+    assert B.pl_pile_prefill(A2, A, 0, 64, 333, None, 1000, 5, None) == B.PL_EINVAL
+    assert B.pl_pile_prefill(A2, A, 9, 64, 333, None, 1000, 5, None) == B.PL_EINVAL
+    assert B.pl_pile_prefill(A2, A, 4, 64, 334, None, 1000, 5, None) == B.PL_EINVAL
+    assert "t = 1002" in B.last_error()
+    assert B.pl_pile_prefill(ctypes.c_void_p(0x10000 + 64 * 4), A, 3, 64, 333, None, 1000, 5, None) == B.PL_EINVAL
+    assert "overlap" in B.last_error()
+    assert B.pl_pile_prefill(A2, A, 3, 64, 333, None, 999, 5, None) == B.PL_EINVAL
+    # lerp: null, sizes, overlap of out with an input
+    assert B.pl_lerp_points(None, A2, 16, 12, A, None) == B.PL_EINVAL
+    assert B.pl_lerp_points(A2, A2, 0, 12, A, None) == B.PL_EINVAL
+    assert B.pl_lerp_points(A2, A2, 16, 0, A, None) == B.PL_EINVAL
+    assert B.pl_lerp_points(A, A2, 16, 12, ctypes.c_void_p(0x10000 - 64), None) == B.PL_EINVAL
+    assert "overlap" in B.last_error()
 
 
 @pytest.mark.parametrize("kw", [

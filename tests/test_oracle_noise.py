@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 from scipy import stats
 
-from oracle import (philox4x64, uniform24, window_noise, staircase_prefill, lerp_points,
+from oracle import (philox4x64, uniform24, window_noise, noise_at, staircase_prefill, lerp_points,
                     ddim_step, sd_scaled_linear_alphas_cumprod)
 
 MASK = (1 << 64) - 1
@@ -90,6 +90,7 @@ def test_window_noise_is_standard_normal():
 def test_window_noise_ragged_length_is_a_prefix():
     full = window_noise(9, 2, 40)
     assert np.array_equal(window_noise(9, 2, 37), full[:37])
+    assert np.array_equal(noise_at(9, 2, [39, 0, 17, 17]), full[[39, 0, 17, 17]])
 
 
 def test_staircase_prefill_recovers_reference_through_ddim():
