@@ -184,9 +184,11 @@ def main():
     log(f"inputs ready in {time.perf_counter() - t0:.1f}s (m={m})")
 
     pile = B.Pile(4, 333)
+    next_window = [4]  # ids 0..2 prefilled, 3 enters with the first round
 
     def step(events=None):
-        # the round's 16 attention layers, then the DDIM step and the drift check
+        # the round's 16 attention layers, then the DDIM step (which also draws
+        # the next window's noise into the leaving window's slot) and the drift check
         for li, lay in enumerate(layers):
             if events is not None:
                 events[li][0].record()
@@ -194,7 +196,9 @@ def main():
             if events is not None:
                 events[li][1].record()
         _, t_slot, emit = pile.begin_round()
-        B.pyramid_ddim_step(x_t, eps, t_slot, x_prev=x_prev, x0_out=x0, emit_window=emit)
+        B.pyramid_ddim_step(x_t, eps, t_slot, x_prev=x_prev, x0_out=x0, emit_window=emit,
+                            roll=(SEED, next_window[0]))
+        next_window[0] += 1
         pile.end_round()
         B.motion_bank_min_l2(mq, mb, 17.0, out=md)
 
@@ -251,6 +255,11 @@ def main():
 
     t_slot = [0, 333, 666, 999]
     ddim_us = time_it(lambda: B.pyramid_ddim_step(x_t, eps, t_slot, x_prev=x_prev, x0_out=x0, emit_window=0))
+    roll_us = time_it(lambda: B.pyramid_ddim_step(x_t, eps, t_slot, x_prev=x_prev, x0_out=x0, emit_window=0,
+                                                  roll=(SEED, 9)))
+    prefill_ref = torch.randn(4 * 4 * 64 * 64, device=dev)
+    prefill_out = torch.empty((3, prefill_ref.numel()), device=dev)
+    prefill_us = time_it(lambda: B.pile_prefill(prefill_ref, 3, SEED, out=prefill_out))
     motion_us = time_it(lambda: B.motion_bank_min_l2(mq, mb, 17.0, out=md))
 
     # ---- DDIM bandwidth sweep: rotating working sets well beyond the 256 MB cache ------------
@@ -334,7 +343,9 @@ def main():
             "algorithmic_bytes_per_launch": dom_l["bytes"],
             "avg_launch_us": round(1e3 * dom_ms, 2),
         },
-        "ddim": {"us_at_round_shape": round(ddim_us, 2), "bytes_at_round_shape": 3407872, "sweep": sweep},
+        "ddim": {"us_at_round_shape": round(ddim_us, 2), "bytes_at_round_shape": 3407872,
+                 "us_with_roll_at_round_shape": round(roll_us, 2), "sweep": sweep},
+        "pile_prefill_us": round(prefill_us, 2),
         "motion_us": round(motion_us, 2),
         "layers": layer_report,
         "cpu_baseline": cpu,

@@ -23,6 +23,9 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr int kDdimThreads = 256;
 constexpr int kDdimUnroll = 4;  // float4 per thread per grid-stride step
 
+// ROLL: the emitted window's x_prev slot takes the next window's noise (a
+// separate instantiation, so the plain step carries none of that code).
+template <bool ROLL>
 __global__ void __launch_bounds__(kDdimThreads)
 ddim_vec4_kernel(const f4v* x_t, const f4v* eps, f4v* x_prev,
                  f4v* __restrict__ x0_out, int64_t n4_per_window, int emit_window, DdimLaunch cf) {
@@ -49,7 +52,7 @@ ddim_vec4_kernel(const f4v* x_t, const f4v* eps, f4v* x_prev,
       const int64_t i = base + (int64_t)u * kDdimThreads;
       if (i < n4_per_window) {
         f4v pv;
-        if (emit && cf.roll) {
+        if (ROLL && emit) {
           // the leaving window's slot becomes next round's new window: its own
           // x_prev is never used, so the slot takes the new window's noise
           // (float4 i of the window is noise block i)
@@ -71,6 +74,7 @@ ddim_vec4_kernel(const f4v* x_t, const f4v* eps, f4v* x_prev,
 }
 
 // Scalar variant for sizes or pointers that do not allow 16 B accesses.
+template <bool ROLL>
 __global__ void __launch_bounds__(kDdimThreads)
 ddim_scalar_kernel(const float* x_t, const float* eps, float* x_prev,
                    float* __restrict__ x0_out, int64_t n_per_window, int emit_window, DdimLaunch cf) {
@@ -82,7 +86,7 @@ ddim_scalar_kernel(const float* x_t, const float* eps, float* x_prev,
        i += (int64_t)gridDim.x * kDdimThreads) {
     const float xv = x_t[off + i], ev = eps[off + i];
     if (emit) x0_out[i] = fmaf(c, xv, d * ev);
-    if (emit && cf.roll)
+    if (ROLL && emit)
       x_prev[off + i] = normal4(cf.seed, cf.new_id, (uint64_t)(i >> 2))[i & 3];
     else
       x_prev[off + i] = fmaf(a, xv, b * ev);
@@ -106,12 +110,13 @@ hipError_t launch_pyramid_ddim(const DdimLaunch& a, hipStream_t stream) {
   if (bx < 1) bx = 1;
   dim3 grid((unsigned)bx, (unsigned)a.W);
   if (vec) {
-    hipLaunchKernelGGL(ddim_vec4_kernel, grid, dim3(kDdimThreads), 0, stream,
+    hipLaunchKernelGGL(a.roll ? ddim_vec4_kernel<true> : ddim_vec4_kernel<false>, grid, dim3(kDdimThreads), 0, stream,
                        reinterpret_cast<const f4v*>(a.x_t), reinterpret_cast<const f4v*>(a.eps),
                        reinterpret_cast<f4v*>(a.x_prev), reinterpret_cast<f4v*>(a.x0_out),
                        a.elems_per_window / 4, a.emit_window, a);
   } else {
-    hipLaunchKernelGGL(ddim_scalar_kernel, grid, dim3(kDdimThreads), 0, stream, a.x_t, a.eps, a.x_prev,
+    hipLaunchKernelGGL(a.roll ? ddim_scalar_kernel<true> : ddim_scalar_kernel<false>, grid, dim3(kDdimThreads), 0,
+                       stream, a.x_t, a.eps, a.x_prev,
                        a.x0_out, a.elems_per_window, a.emit_window, a);
   }
   return hipGetLastError();
