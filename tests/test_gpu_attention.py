@@ -199,3 +199,40 @@ def test_zero_queries_mean_of_values_at_scale(B):
         mean = vals.mean(axis=0)
         err = np.abs(got[f].astype(np.float64) - mean[None, :])
         assert err.max() <= 1e-2 and err.mean() <= 1e-3, (err.max(), err.mean())
+
+
+# ---- bounded-context key lists (sink + sliding window, PR-Sink) -------------------
+def _chunk_stream(seed, n_chunks, L, C):
+    rng = np.random.default_rng(seed)
+    f16 = lambda *s: rng.standard_normal(s, dtype=np.float32).astype(np.float16)
+    return [(f16(L, C), f16(L, C)) for _ in range(n_chunks)], (f16(L, C), f16(L, C))
+
+
+@pytest.mark.parametrize("scheme,d,L,H", [("sink_window", 40, 192, 2), ("sink_window", 80, 100, 1),
+                                          ("pr_sink", 40, 128, 2), ("pr_sink", 160, 64, 1)])
+def test_bounded_context_segments(B, scheme, d, L, H):
+    """A chunk's attention over the key list a bounded-context scheme picks:
+    current chunk + cached chunks + reference, one call, against the oracle."""
+    from streaming_diffusion_portrait_amd.context import sink_window_ids, pr_sink_ids, context_segments
+    say("bounded context", scheme, d, L, H)
+    C = H * d
+    chunks, ref = _chunk_stream(zlib.crc32(scheme.encode()) + d, 12, L, C)
+    current = 11
+    rng = np.random.default_rng(d)
+    q = rng.standard_normal((1, L, C), dtype=np.float32).astype(np.float16)
+    if scheme == "sink_window":
+        ids = sink_window_ids(current)
+    else:
+        # dynamic sink: the earlier chunk whose pose embedding is nearest (GPU min-L2 check)
+        # among four candidate chunks (3..6), the way the motion bank is searched
+        poses = rng.standard_normal((current, 512), dtype=np.float32)
+        query_pose = poses[5] + 0.01 * rng.standard_normal(512, dtype=np.float32)
+        _, am, _ = B.motion_bank_min_l2(dev(query_pose), dev(poses[3:7]), 17.0)
+        ids = pr_sink_ids(current, dynamic=3 + int(am.cpu().numpy()[0]))
+        assert 5 in ids
+    cur = (chunks[current][0][None], chunks[current][1][None])
+    segs_np = context_segments(cur, {i: chunks[i] for i in range(current)}, ids, ref)
+    assert len(segs_np) <= 8
+    segs = [(k, v, k.ndim == 2) for k, v in segs_np]
+    got = run_gpu(B, q, segs, H)
+    assert_attn_close(got, refbank_attention(q, segs, H), f"{scheme} d={d}")
