@@ -62,6 +62,7 @@
 //     v_dot2_f32_f16 on the packed probabilities (other head dims).
 #include "pl_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace pl {
@@ -480,6 +481,7 @@ __device__ __forceinline__ void tile_step(const char* smem, int kt, int valid, b
                                           const LaneCtx& lc) {
 #pragma unroll
   for (int kb = 0; kb < C::NKB; ++kb) {
+    if (kb > 0 && valid <= 32 * kb) break;  // a tile's last block holds no key (short segments)
     f16v s[C::NQB];
     qk_block<C>(smem, kt + kb * C::KBLK, ws, lc, s);
     h8 va[C::NDT];
@@ -851,7 +853,9 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
       }
     }
 
-    if (exact_all) return false;
+    // Tiles taken with exact maxima cannot overflow: only a pass that froze the
+    // offset for a later tile needs the check (and its two barriers).
+    if (exact_all || !fast || ntiles == 1) return false;
     // A frozen offset is only unsafe if some probability left the fp16 range:
     // then a row sum is inf or NaN.  Decide for the whole workgroup.
     bool bad = false;
@@ -911,6 +915,149 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
   }
 }
 
+// ---- short contexts: one segment of at most one tile -------------------------
+//
+// The expression cross-attention of the denoiser (PersonaLive, section
+// 三条条件通路: the 512-d expression embedding becomes 32 tokens that the
+// Spatial_Cross blocks attend to) and the CLIP one (a single 1x768 token)
+// have a key sequence of at most one tile.  There the work is reading Q and
+// writing O; each workgroup stages its (frame, head)'s keys once and its waves
+// walk many 32-query blocks, loading the next block's Q while the current one
+// is computed, so the memory latency overlaps the arithmetic.
+
+template <class C>
+__device__ __forceinline__ void load_q_block(const KParams& p, const _Float16* qb_, int row, const LaneCtx& lc,
+                                             h8 (&qf)[C::KST]) {
+#pragma unroll
+  for (int st = 0; st < C::KST; ++st) {
+    const int col = 16 * st + 8 * lc.h;
+    h8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (row < p.Lq && col < C::D) v = *reinterpret_cast<const h8*>(qb_ + (int64_t)row * p.q_ld + col);
+    qf[st] = v;
+  }
+}
+
+#ifndef PL_SHORT_WGS
+#define PL_SHORT_WGS 1024  // workgroups a short-context launch aims for (4 per CU)
+#endif
+
+template <class C>
+__global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams p, int nsplit) {
+  static_assert(C::NQB == 1, "one 32-query block per step");
+  __shared__ __attribute__((aligned(16))) char smem[C::LDSB];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  LaneCtx lc;
+  lc.lane = tid & 63;
+  lc.h = lc.lane >> 5;
+  lc.c16 = lc.lane & 15;
+  lc.g = lc.lane >> 4;
+  const int c32 = lc.lane & 31;
+
+  // workgroup -> (frame, split, head), head fastest; ids dealt round-robin to
+  // the 8 XCDs are remapped so that each XCD takes a contiguous range: all
+  // heads of the same query rows then meet in one L2, which merges their
+  // column slices of each Q and O line.
+  const int total = p.H * p.F * nsplit;
+  int lid = blockIdx.x;
+  if ((total & 7) == 0) lid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int hd = lid % p.H;
+  const int fs = lid / p.H;
+  const int f = fs / nsplit;
+  const int split = fs - f * nsplit;
+
+  if (C::ONES) {
+    for (int i = tid >> 6; i < 2 * C::NBUF; i += C::W) {
+      h8 one = {0, 0, 0, 0, 0, 0, 0, 0};
+      one[0] = (_Float16)1.0f;
+      *reinterpret_cast<h8*>(smem + i * C::TILEB + C::CPR * C::PLB + 16 * lc.lane) = one;
+    }
+  }
+  lc.krow_off = c32 * 16 + lc.h * C::PLB;
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    lc.vrow_off[r] = (vrow(lc.g) + 16 * r + (lc.c16 >> 2)) * 16 + ((lc.c16 & 3) >> 1) * C::PLB + 8 * (lc.c16 & 1);
+
+  // the whole key sequence is one (possibly ragged) tile
+  Copier<C> cp;
+  cp.s = 0;
+  cp.off = 0;
+  cp.issued = 0;
+  issue_tile<C>(p, smem, cp, f, hd, wave, lc.lane);
+  const int valid = (int)min((int64_t)C::BN, p.seg[0].len);
+
+  // this wave's query blocks: split s takes every nsplit-th group of W blocks
+  const int nblk = (p.Lq + 31) / 32;
+  const _Float16* qb_ = p.q + (int64_t)f * p.q_fs + (int64_t)hd * C::D;
+  _Float16* ob = p.o + (int64_t)f * p.o_fs + (int64_t)hd * C::D;
+  const int step = nsplit * C::W;
+  int blk = split * C::W + wave;
+  h8 qn[C::KST];
+  if (blk < nblk) load_q_block<C>(p, qb_, 32 * blk + c32, lc, qn);
+  wait_vm(0);
+  __syncthreads();  // the tile (and the constant plane) is in LDS
+
+  WaveState<C> ws;
+  for (; blk < nblk; blk += step) {
+#pragma unroll
+    for (int st = 0; st < C::KST; ++st) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ws.qf[0][st][e] = (_Float16)((float)qn[st][e] * p.c2);
+    }
+    if (blk + step < nblk) load_q_block<C>(p, qb_, 32 * (blk + step) + c32, lc, qn);  // next block, in flight
+    ws.mrun[0] = 0.f;
+    ws.lsum[0] = 0.f;
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp)
+#pragma unroll
+      for (int t = 0; t < C::NDT; ++t) ws.oacc[0][grp][t] = (f4){0.f, 0.f, 0.f, 0.f};
+    tile_step<C, false>(smem, 0, valid, true, ws, lc);
+
+    // normalise and write O (fp16, round to nearest even)
+    float tot = 0.f;
+    if (!C::ONES) tot = ws.lsum[0] + __shfl_xor(ws.lsum[0], 32, 64);
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+      float l;
+      if (C::ONES) {
+        constexpr int tl = C::D / 16, gl = (C::D % 16) / 4, rl = C::D % 4;
+        l = __shfl(ws.oacc[0][grp][tl][rl], 16 * gl + lc.c16, 64);
+      } else {
+        l = __shfl(tot, 16 * grp + lc.c16, 64);
+      }
+      const float inv = 1.0f / l;
+      const int row = 32 * blk + 16 * grp + lc.c16;
+      if (row < p.Lq) {
+#pragma unroll
+        for (int t = 0; t < C::NDT; ++t) {
+          const int col = 16 * t + 4 * lc.g;
+          if (col < C::D) {
+            h4 out;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out[r] = (_Float16)(ws.oacc[0][grp][t][r] * inv);
+            *reinterpret_cast<h4*>(ob + (int64_t)row * p.o_ld + col) = out;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int D, int MINB>
+hipError_t launch_short(const KParams& kp, hipStream_t stream) {
+  using C = Cfg<D, 1, 2, 2, MINB, false, 4>;
+  KParams p = kp;
+  const int64_t base = (int64_t)p.F * p.H;
+  // about four workgroups per CU in total, each wave walking one or more blocks
+  const int nblk = (p.Lq + 31) / 32;
+  int nsplit = (int)std::max<int64_t>(1, (int64_t)PL_SHORT_WGS / std::max<int64_t>(base, 1));
+  nsplit = std::min(nsplit, std::max(1, nblk / C::W));
+  if (base * nsplit > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(short_ctx_kernel<C>, dim3((unsigned)(base * nsplit)), dim3(C::THREADS), 0, stream, p, nsplit);
+  return hipGetLastError();
+}
+
 template <int D, int NQB, int NKB, int NBUF, int MINB, bool PIPE, int W>
 hipError_t launch_cfg(const KParams& kp, hipStream_t stream) {
   using C = Cfg<D, NQB, NKB, NBUF, MINB, PIPE, W>;
@@ -941,6 +1088,17 @@ hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream) {
   p.nseg = a.nseg;
   p.c2 = a.scale * kLog2e;
   for (int i = 0; i < PL_MAX_SEGMENTS; ++i) p.seg[i] = a.seg[i];
+  // a single segment of at most one tile: the short-context kernel
+  if (a.nseg == 1 && a.seg[0].len <= 64) {
+    p.nqt = 0;
+    switch (a.d) {
+      case 32: return launch_short<32, 4>(p, stream);
+      case 40: return launch_short<40, 3>(p, stream);
+      case 80: return launch_short<80, 2>(p, stream);
+      case 160: return launch_short<160, 1>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.d) {
     case 32: return launch_cfg<32, 2, 2, 4, 2, true, 4>(p, stream);
     case 40: return launch_cfg<40, 2, 2, 4, 2, true, 4>(p, stream);

@@ -236,3 +236,48 @@ def test_bounded_context_segments(B, scheme, d, L, H):
     segs = [(k, v, k.ndim == 2) for k, v in segs_np]
     got = run_gpu(B, q, segs, H)
     assert_attn_close(got, refbank_attention(q, segs, H), f"{scheme} d={d}")
+
+
+# ---- short contexts: the expression (32 tokens per frame) and CLIP (1 token) ----
+SHORT = [
+    # (name, d, F, L, H, seglen, shared)
+    ("expr d40 small", 40, 3, 300, 2, 32, False),
+    ("expr d80 small", 80, 2, 130, 2, 32, False),
+    ("expr d160 small", 160, 2, 70, 1, 32, False),
+    ("expr d32 small", 32, 2, 257, 2, 32, False),
+    ("clip d40 small", 40, 2, 100, 2, 1, True),
+    ("ctx 64 d40", 40, 2, 1000, 1, 64, True),
+    ("ctx 50 d80 ragged rows", 80, 1, 37, 2, 50, False),
+]
+
+
+@pytest.mark.parametrize("name,d,F,L,H,seglen,shared", SHORT, ids=[c[0] for c in SHORT])
+def test_short_context_full(B, name, d, F, L, H, seglen, shared):
+    say("attn short", name)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    C = H * d
+    q = rand16(rng, F, L, C)
+    shape = (seglen, C) if shared else (F, seglen, C)
+    segs = [(rand16(rng, *shape), rand16(rng, *shape), shared)]
+    got = run_gpu(B, q, segs, H)
+    ref = refbank_attention(q, segs, H)
+    assert_attn_close(got, ref, name)
+    if seglen == 1:  # one key: every output row is that key's value row
+        v = segs[0][1].astype(np.float64)
+        assert np.allclose(got.astype(np.float64), np.broadcast_to(v, got.shape), atol=1e-3)
+
+
+@pytest.mark.parametrize("L,C", [(4096, 320), (1024, 640), (256, 1280), (64, 1280)])
+def test_short_context_workload_sampled(B, L, C):
+    """Expression cross-attention at each level: 16 frames, 8 heads, 32 keys per frame."""
+    say("attn expression level", L, C)
+    H, F = 8, 16
+    rng = np.random.default_rng(L + C)
+    q = rand16(rng, F, L, C)
+    segs = [(rand16(rng, F, 32, C), rand16(rng, F, 32, C), False)]
+    got = run_gpu(B, q, segs, H)
+    d = C // H
+    rows = np.unique(np.concatenate([rng.choice(L, size=min(64, L), replace=False), [0, L - 1]]))
+    for f, h in [(0, 0), (5, 3), (F - 1, H - 1)]:
+        ref = refbank_attention(q, segs, H, frames=[f], head_list=[h], rows=rows)[(f, h)]
+        assert_attn_close(got[f][rows][:, h * d:(h + 1) * d], ref, f"expr L={L} f={f} h={h}")
