@@ -257,6 +257,24 @@ def main():
     ddim_us = time_it(lambda: B.pyramid_ddim_step(x_t, eps, t_slot, x_prev=x_prev, x0_out=x0, emit_window=0))
     roll_us = time_it(lambda: B.pyramid_ddim_step(x_t, eps, t_slot, x_prev=x_prev, x0_out=x0, emit_window=0,
                                                   roll=(SEED, 9)))
+    # expression cross-attention (32 tokens per frame, same boundary call, short-context
+    # kernel) at each level: HBM-bound, so bytes = Q + O + K/V
+    short_ctx = []
+    for L, C in ((4096, 320), (1024, 640), (256, 1280), (64, 1280)):
+        g = torch.Generator(device=dev).manual_seed(L)
+        sq = torch.randn(F, L, C, device=dev, generator=g).half()
+        sk = torch.randn(F, 32, C, device=dev, generator=g).half()
+        sv = torch.randn(F, 32, C, device=dev, generator=g).half()
+        so = torch.empty_like(sq)
+        scall = B.PreparedAttn(sq, [(sk, sv)], H, so)
+        s_us = time_it(scall, n=50)
+        s_bytes = (2 * F * L * C + 2 * F * 32 * C) * 2
+        short_ctx.append(dict(L=L, C=C, keys=32, us=round(s_us, 2), bytes=s_bytes,
+                              GBps=round(s_bytes / (s_us * 1e-6) / 1e9, 1),
+                              frac_hbm_peak=round(s_bytes / (s_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 3)))
+        del sq, sk, sv, so, scall
+    log("  expression cross-attention (32 keys/frame): " +
+        ", ".join(f"L={r['L']} {r['us']:.1f} us {r['GBps']:.0f} GB/s" for r in short_ctx))
     prefill_ref = torch.randn(4 * 4 * 64 * 64, device=dev)
     prefill_out = torch.empty((3, prefill_ref.numel()), device=dev)
     prefill_us = time_it(lambda: B.pile_prefill(prefill_ref, 3, SEED, out=prefill_out))
@@ -346,6 +364,7 @@ def main():
         "ddim": {"us_at_round_shape": round(ddim_us, 2), "bytes_at_round_shape": 3407872,
                  "us_with_roll_at_round_shape": round(roll_us, 2), "sweep": sweep},
         "pile_prefill_us": round(prefill_us, 2),
+        "expression_cross_attention": short_ctx,
         "motion_us": round(motion_us, 2),
         "layers": layer_report,
         "cpu_baseline": cpu,
