@@ -19,6 +19,9 @@ juhe.plus, "PersonaLive" for short, and the hysenlabs repository review):
   (PersonaLive, section "抗身份漂移的补丁" / anti identity-drift patch).
 * ``pile``       -- the ``latents_pile`` queue state machine
   (PersonaLive, section "流式金字塔去噪").
+* ``linear``     -- the projections either side of the attention
+  (PersonaLive, section "三条条件通路": the bank holds hidden states that the
+  layer projects into keys and values).
 * ``noise``      -- the pile's device-side roll: counter-based window noise,
   the staircase prefill and the first frames' motion interpolation
   (PersonaLive, sections "流式金字塔去噪", "首帧怎么办" and the TensorRT
@@ -42,6 +45,7 @@ from .ddim import (
 )
 from .motion import motion_bank_min_l2
 from .pile import PyramidPile
+from .linear import linear
 from .noise import philox4x64, uniform24, window_noise, noise_at, staircase_prefill, lerp_points
 
 __all__ = [
@@ -54,6 +58,7 @@ __all__ = [
     "pyramid_ddim_step",
     "motion_bank_min_l2",
     "PyramidPile",
+    "linear",
     "philox4x64",
     "uniform24",
     "window_noise",
