@@ -38,7 +38,7 @@ typedef int32_t pl_status;
 #define PL_EUNSUPPORTED 2  /* valid in principle but not implemented (head dim, alignment) */
 #define PL_EDEVICE 3       /* the HIP runtime reported an error at launch */
 
-#define PL_ABI_VERSION 2
+#define PL_ABI_VERSION 3
 #define PL_MAX_SEGMENTS 8       /* key segments per attention call: self + reference + anchors (5 used) */
 #define PL_MAX_WINDOWS 8        /* windows per pile (the pages use 4) */
 #define PL_MAX_MOTION_BANK 4    /* reference embedding + at most 3 anchors */
@@ -107,6 +107,33 @@ pl_status pl_refbank_attn(const void* q, int64_t q_ld, int64_t q_frame_stride,
                           int32_t F, int32_t Lq, int32_t H, int32_t d,
                           const pl_kv_segment* segs, int32_t nseg, float scale,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Projections either side of the attention
+ *
+ * PersonaLive, section 三条条件通路: the bank stores each reference layer's
+ * hidden states and the denoiser attends to them next to its own keys and
+ * values, so the bank's keys and values are that layer's linear projections
+ * of them (projecting each entry once, when it is written, gives the same
+ * keys as projecting the joined sequence: a projection acts on each token
+ * separately).  The denoiser's to_q / to_k / to_v / to_out are linear layers
+ * of the same kind.
+ *
+ *   y[m][n] = sum_k x[m][k] * w[n][k] (+ bias[n]), fp16 in and out, fp32
+ *   accumulation, output rounded to nearest even.
+ *   x     device fp16 [M][x_ld], x_ld >= K, multiple of 8, 16-byte aligned.
+ *   w     device fp16 [N][w_ld] (out features x in features, as linear layers
+ *         store it), w_ld >= K, multiple of 8, 16-byte aligned.  A fused
+ *         q/k/v weight [3C][C] gives y = [q | k | v], whose column slices are
+ *         valid pl_refbank_attn operands (row stride 3C).
+ *   bias  device fp32 [N] or NULL.
+ *   y     device fp16 [M][y_ld], y_ld >= N, multiple of 4, 8-byte aligned; must
+ *         not overlap x or w.
+ *   M in 1..2^31; N a multiple of 64; K a multiple of 16 (PL_EUNSUPPORTED
+ *   otherwise).
+ * ------------------------------------------------------------------------ */
+pl_status pl_linear(const void* x, int64_t x_ld, const void* w, int64_t w_ld, const float* bias, void* y,
+                    int64_t y_ld, int64_t M, int32_t N, int32_t K, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * Per-window DDIM step of the latents pile

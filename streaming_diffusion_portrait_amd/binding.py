@@ -35,6 +35,7 @@ EXPORTED = (
     "pl_window_noise",
     "pl_pile_prefill",
     "pl_lerp_points",
+    "pl_linear",
     "pl_motion_bank_min_l2",
     "pl_pile_init",
     "pl_pile_begin_round",
@@ -112,6 +113,8 @@ def load():
     lib.pl_pile_prefill.argtypes = [vp, vp, i32, i64, i32, ctypes.POINTER(f64), i32, u64, vp]
     lib.pl_lerp_points.restype = i32
     lib.pl_lerp_points.argtypes = [vp, vp, i64, i32, vp, vp]
+    lib.pl_linear.restype = i32
+    lib.pl_linear.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i32, i32, vp]
     lib.pl_motion_bank_min_l2.restype = i32
     lib.pl_motion_bank_min_l2.argtypes = [vp, i32, vp, i32, i32, f32, vp, vp, vp, vp]
     lib.pl_pile_init.restype = i32
@@ -165,6 +168,10 @@ def pl_pile_prefill(*args):
 
 def pl_lerp_points(*args):
     return load().pl_lerp_points(*args)
+
+
+def pl_linear(*args):
+    return load().pl_linear(*args)
 
 
 def pl_motion_bank_min_l2(*args):
@@ -342,6 +349,38 @@ def pile_prefill(ref, n_windows, seed, step_len=333, alphas_cumprod=None, out=No
     _check("pl_pile_prefill", pl_pile_prefill(ctypes.c_void_p(ref.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                                               int(n_windows), per, int(step_len), ab_ptr, T, int(seed),
                                               _stream_ptr(stream)))
+    return out
+
+
+def linear(x, w, bias=None, out=None, stream=None):
+    """y = x W^T (+ bias) (see ``pl_linear``).
+
+    ``x``: fp16 device ``[M, K]`` (or ``[..., K]``, flattened over the leading
+    axes; rows may be strided); ``w``: fp16 ``[N, K]``; ``bias``: fp32 ``[N]``
+    or None.  Returns ``out`` ``[..., N]`` (allocated if None).
+    """
+    _need(x, torch.float16, "x")
+    _need(w, torch.float16, "w")
+    if x.stride(-1) != 1 or w.dim() != 2 or w.stride(-1) != 1:
+        raise ValueError("x and w need unit stride in their last dimension; w must be [N, K]")
+    lead = x.shape[:-1]
+    K = x.shape[-1]
+    x2 = x.reshape(-1, K) if x.dim() != 2 else x
+    M = x2.shape[0]
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("w must be [N, K] with x's K")
+    if out is None:
+        out = torch.empty((*lead, N), dtype=torch.float16, device=x.device)
+    _need(out, torch.float16, "out")
+    y2 = out.reshape(-1, N) if out.dim() != 2 else out
+    if bias is not None:
+        _need(bias, torch.float32, "bias")
+        if not bias.is_contiguous() or bias.numel() != N:
+            raise ValueError("bias must be contiguous [N]")
+    _check("pl_linear", pl_linear(ctypes.c_void_p(x2.data_ptr()), x2.stride(0), ctypes.c_void_p(w.data_ptr()),
+                                  w.stride(0), ctypes.c_void_p(bias.data_ptr()) if bias is not None else None,
+                                  ctypes.c_void_p(y2.data_ptr()), y2.stride(0), M, N, K, _stream_ptr(stream)))
     return out
 
 

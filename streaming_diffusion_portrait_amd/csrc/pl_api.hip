@@ -275,6 +275,41 @@ pl_status pl_pile_prefill(const float* ref, float* pile, int32_t n_windows, int6
   return device_status(pl::launch_noise_affine(a, static_cast<hipStream_t>(stream)), "pl_pile_prefill launch");
 }
 
+pl_status pl_linear(const void* x, int64_t x_ld, const void* w, int64_t w_ld, const float* bias, void* y,
+                    int64_t y_ld, int64_t M, int32_t N, int32_t K, void* stream) {
+  if (!x || !w || !y) return fail(PL_EINVAL, "pl_linear: x, w and y must be non-null");
+  if (M < 1 || N < 1 || K < 1) return fail(PL_EINVAL, "pl_linear: M, N and K must be >= 1");
+  if (M > (int64_t(1) << 31)) return fail(PL_EINVAL, "pl_linear: M must be <= 2^31");
+  if (N % 64) return fail(PL_EUNSUPPORTED, "pl_linear: N must be a multiple of 64 (got %d)", N);
+  if (K % 16) return fail(PL_EUNSUPPORTED, "pl_linear: K must be a multiple of 16 (got %d)", K);
+  if (x_ld < K || w_ld < K || y_ld < N) return fail(PL_EINVAL, "pl_linear: x_ld, w_ld >= K and y_ld >= N required");
+  if (x_ld % 8 || w_ld % 8 || y_ld % 4)
+    return fail(PL_EUNSUPPORTED, "pl_linear: x_ld and w_ld must be multiples of 8 elements, y_ld of 4");
+  if (!aligned16(x) || !aligned16(w) || (reinterpret_cast<uintptr_t>(y) & 7))
+    return fail(PL_EUNSUPPORTED, "pl_linear: x and w must be 16-byte aligned, y 8-byte aligned");
+  if (bias && (reinterpret_cast<uintptr_t>(bias) & 3)) return fail(PL_EUNSUPPORTED, "pl_linear: bias must be 4-byte aligned");
+  // y must not overlap x or w (the rows of y are written while others are read)
+  const char* y0 = static_cast<const char*>(y);
+  const char* y1 = y0 + ((M - 1) * y_ld + N) * 2;
+  const char* x0 = static_cast<const char*>(x);
+  const char* x1 = x0 + ((M - 1) * x_ld + K) * 2;
+  const char* w0 = static_cast<const char*>(w);
+  const char* w1 = w0 + ((int64_t)(N - 1) * w_ld + K) * 2;
+  if ((y0 < x1 && x0 < y1) || (y0 < w1 && w0 < y1)) return fail(PL_EINVAL, "pl_linear: y overlaps x or w");
+  pl::LinearLaunch a;
+  a.x = static_cast<const _Float16*>(x);
+  a.w = static_cast<const _Float16*>(w);
+  a.bias = bias;
+  a.y = static_cast<_Float16*>(y);
+  a.x_ld = x_ld;
+  a.w_ld = w_ld;
+  a.y_ld = y_ld;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  return device_status(pl::launch_linear(a, static_cast<hipStream_t>(stream)), "pl_linear launch");
+}
+
 pl_status pl_lerp_points(const float* a, const float* b, int64_t D, int32_t n, float* out, void* stream) {
   if (!a || !b || !out) return fail(PL_EINVAL, "pl_lerp_points: pointers must be non-null");
   if (D < 1 || D > (int64_t(1) << 40)) return fail(PL_EINVAL, "pl_lerp_points: D must be in [1, 2^40]");

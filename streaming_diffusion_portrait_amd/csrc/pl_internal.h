@@ -63,6 +63,19 @@ struct NoiseLaunch {
 hipError_t launch_noise_affine(const NoiseLaunch& a, hipStream_t stream);
 hipError_t launch_lerp_points(const float* a, const float* b, int64_t D, int n, float* out, hipStream_t stream);
 
+// ---- projections: y = x W^T (+ b) ----------------------------------------------
+struct LinearLaunch {
+  const _Float16* x;  // [M][x_ld]
+  const _Float16* w;  // [N][w_ld] (out features x in features)
+  const float* bias;  // [N] or nullptr
+  _Float16* y;        // [M][y_ld]
+  int64_t x_ld, w_ld, y_ld;
+  int64_t M;
+  int32_t N, K;       // N % 64 == 0, K % 16 == 0
+};
+
+hipError_t launch_linear(const LinearLaunch& a, hipStream_t stream);
+
 // ---- motion-bank min-L2 -------------------------------------------------------
 struct MotionLaunch {
   const float* query;

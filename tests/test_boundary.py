@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pl_abi_version() == 2
+    assert lib.pl_abi_version() == 3
     assert [B.status_name(s) for s in range(4)] == ["PL_OK", "PL_EINVAL", "PL_EUNSUPPORTED", "PL_EDEVICE"]
     assert B.status_name(99) == "PL_UNKNOWN"
 
@@ -137,6 +137,23 @@ def test_ddim_roll_rejects(lib, kw):
                                      args["step"], args["ab"], args["T"], args["fin"], args["emit"], 7, 11, None)
     assert st == B.PL_EINVAL
     assert B.last_error() != ""
+
+
+def test_linear_rejects(lib):
+    ok = dict(x=A, xld=320, w=A2, wld=320, b=None, y=ctypes.c_void_p(0x40000), yld=960, M=100, N=960, K=320)
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return B.pl_linear(a["x"], a["xld"], a["w"], a["wld"], a["b"], a["y"], a["yld"], a["M"], a["N"], a["K"], None)
+    assert call(x=None) == B.PL_EINVAL
+    assert call(M=0) == B.PL_EINVAL
+    assert call(N=100) == B.PL_EUNSUPPORTED
+    assert call(K=40) == B.PL_EUNSUPPORTED
+    assert call(xld=300) == B.PL_EINVAL
+    assert call(yld=900) == B.PL_EINVAL
+    assert call(x=MIS) == B.PL_EUNSUPPORTED
+    assert call(y=ctypes.c_void_p(0x10000 + 2 * 320)) == B.PL_EINVAL  # y overlaps x
+    assert "overlap" in B.last_error()
 
 
 def test_noise_prefill_lerp_reject(lib):
