@@ -126,7 +126,7 @@ pl_status pl_refbank_attn(const void* q, int64_t q_ld, int64_t q_frame_stride,
  *         store it), w_ld >= K, multiple of 8, 16-byte aligned.  A fused
  *         q/k/v weight [3C][C] gives y = [q | k | v], whose column slices are
  *         valid pl_refbank_attn operands (row stride 3C).
- *   bias  device fp32 [N] or NULL.
+ *   bias  device fp32 [N], 16-byte aligned, or NULL.
  *   y     device fp16 [M][y_ld], y_ld >= N, multiple of 4, 8-byte aligned; must
  *         not overlap x or w.
  *   M in 1..2^31; N a multiple of 64; K a multiple of 16 (PL_EUNSUPPORTED

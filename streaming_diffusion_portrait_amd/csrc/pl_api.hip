@@ -287,7 +287,7 @@ pl_status pl_linear(const void* x, int64_t x_ld, const void* w, int64_t w_ld, co
     return fail(PL_EUNSUPPORTED, "pl_linear: x_ld and w_ld must be multiples of 8 elements, y_ld of 4");
   if (!aligned16(x) || !aligned16(w) || (reinterpret_cast<uintptr_t>(y) & 7))
     return fail(PL_EUNSUPPORTED, "pl_linear: x and w must be 16-byte aligned, y 8-byte aligned");
-  if (bias && (reinterpret_cast<uintptr_t>(bias) & 3)) return fail(PL_EUNSUPPORTED, "pl_linear: bias must be 4-byte aligned");
+  if (bias && !aligned16(bias)) return fail(PL_EUNSUPPORTED, "pl_linear: bias must be 16-byte aligned");
   // y must not overlap x or w (the rows of y are written while others are read)
   const char* y0 = static_cast<const char*>(y);
   const char* y1 = y0 + ((M - 1) * y_ld + N) * 2;
