@@ -275,6 +275,26 @@ def main():
         del sq, sk, sv, so, scall
     log("  expression cross-attention (32 keys/frame): " +
         ", ".join(f"L={r['L']} {r['us']:.1f} us {r['GBps']:.0f} GB/s" for r in short_ctx))
+    # the projections either side of the attention: fused q/k/v ([3C, C]) and the
+    # output projection ([C, C] + bias) over the 16 frames of each level
+    projections = []
+    for L, C in ((4096, 320), (1024, 640), (256, 1280), (64, 1280)):
+        g = torch.Generator(device=dev).manual_seed(7 * L)
+        px = torch.randn(F * L, C, device=dev, generator=g).half()
+        for pname, N, with_bias in (("qkv", 3 * C, False), ("out", C, True)):
+            pw = (torch.randn(N, C, device=dev, generator=g) / C ** 0.5).half()
+            pb = torch.randn(N, device=dev, generator=g) if with_bias else None
+            py = torch.empty(F * L, N, device=dev, dtype=torch.float16)
+            p_us = time_it(lambda: B.linear(px, pw, pb, out=py), n=50)
+            p_fl = 2 * F * L * N * C
+            p_by = (F * L * C + N * C + F * L * N) * 2
+            projections.append(dict(name=pname, L=L, C=C, N=N, us=round(p_us, 2),
+                                    tflops=round(p_fl / (p_us * 1e-6) / 1e12, 1),
+                                    GBps=round(p_by / (p_us * 1e-6) / 1e9, 1),
+                                    frac_hbm_peak=round(p_by / (p_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 3)))
+            del pw, py
+        del px
+    log("  projections: " + ", ".join(f"{r['name']} L={r['L']} {r['us']:.1f} us" for r in projections))
     prefill_ref = torch.randn(4 * 4 * 64 * 64, device=dev)
     prefill_out = torch.empty((3, prefill_ref.numel()), device=dev)
     prefill_us = time_it(lambda: B.pile_prefill(prefill_ref, 3, SEED, out=prefill_out))
@@ -365,6 +385,7 @@ def main():
                  "us_with_roll_at_round_shape": round(roll_us, 2), "sweep": sweep},
         "pile_prefill_us": round(prefill_us, 2),
         "expression_cross_attention": short_ctx,
+        "projections": projections,
         "motion_us": round(motion_us, 2),
         "layers": layer_report,
         "cpu_baseline": cpu,
