@@ -130,31 +130,35 @@ __global__ void __launch_bounds__(64 * kWaves, 2) linear_kernel(LinearLaunch p, 
 // ---- staged variant (K a multiple of 64) ---------------------------------------
 // The direct loads above touch 32 rows of 32 bytes per instruction, so the
 // memory pipeline, not the matrix core, sets the pace.  Here 64-wide K chunks
-// of the workgroup's x rows and 64 W rows are copied to LDS with
-// direct-to-LDS loads that read whole 128-byte row segments (8 lanes per
-// row), through a ring of kStages buffers so that the next chunks stream in
-// while one is multiplied; the operands are then read from LDS in
-// matrix-core layout.  The 16-byte chunk c of staged row r sits at slot
-// c ^ ((r / 2) % 8), which puts the 16 rows one read serves on 16 different
-// bank groups.
-#ifndef PL_LINEAR_MW
-#define PL_LINEAR_MW 32
-#endif
-#ifndef PL_LINEAR_STAGES
-#define PL_LINEAR_STAGES 2
-#endif
-constexpr int kSMW = PL_LINEAR_MW;                // rows per wave (32 or 64)
-constexpr int kSJ = kSMW / 32;                    // 32-row products per wave
-constexpr int kSTileM = kSMW * kWaves;            // rows per workgroup
-constexpr int kStages = PL_LINEAR_STAGES;         // ring depth
-constexpr int kChunkK = 64;                       // K per stage
-constexpr int kRowB = kChunkK * 2;                // bytes per staged row
-constexpr int kStageX = kSTileM * kRowB;          // x rows of a stage
-constexpr int kStageB = kStageX + kTileN * kRowB; // + 8 KB of W rows
-constexpr int kDmaPerStage = kStageB / 1024;      // wave-wide 16-byte copies per stage
-constexpr int kDmaPerWave = kDmaPerStage / kWaves;
-static_assert(kDmaPerStage % kWaves == 0, "copies split evenly over the waves");
-static_assert(kDmaPerWave * (kStages - 2) <= 63, "vmcnt range");
+// of the workgroup's x rows and W rows are copied to LDS with direct-to-LDS
+// loads that read whole 128-byte row segments (8 lanes per row), through a
+// ring of STAGES buffers so that the next chunks stream in while one is
+// multiplied; the operands are then read from LDS in matrix-core layout.  The
+// 16-byte chunk c of staged row r sits at slot c ^ ((r / 2) % 8), which puts
+// the 16 rows one read serves on 16 different bank groups.
+//
+// The 4 waves of a workgroup form a WR x (4 / WR) grid; each owns 32 IM rows
+// x 32 IN features, so per 16-wide step it reads IM + IN operands from LDS for
+// IM x IN products.  Larger wave tiles cut the LDS bytes per product (the LDS,
+// not the matrix core, is what small tiles run out of).
+template <int WR_, int IM_, int IN_, int STAGES_>
+struct GemmCfg {
+  static constexpr int WR = WR_, WF = 4 / WR_, IM = IM_, IN = IN_, STAGES = STAGES_;
+  static constexpr int BM = WR * 32 * IM;          // rows per workgroup
+  static constexpr int BN = WF * 32 * IN;          // features per workgroup
+  static constexpr int kChunkK = 64;               // K per stage
+  static constexpr int kRowB = kChunkK * 2;        // bytes per staged row
+  static constexpr int STAGE_X = BM * kRowB;       // x rows of a stage
+  static constexpr int STAGE_B = STAGE_X + BN * kRowB;
+  static constexpr int NCOPY = STAGE_B / 1024;     // wave-wide 16-byte copies per stage (8 rows each)
+  static constexpr int CPW = NCOPY / 4;            // per wave
+  static constexpr int LDS = STAGES * STAGE_B;
+  static constexpr int MINW = LDS <= 80 * 1024 ? 2 : 1;  // workgroups per CU the registers are sized for
+  static_assert(WR == 1 || WR == 2 || WR == 4, "2D grid of 4 waves");
+  static_assert(NCOPY % 4 == 0, "copies split evenly over the waves");
+  static_assert(STAGES >= 2 && CPW * (STAGES - 2) <= 63, "vmcnt range");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -174,122 +178,201 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-__global__ void __launch_bounds__(64 * kWaves, 2) linear_staged_kernel(LinearLaunch p, int n_tiles, int total) {
-  __shared__ __attribute__((aligned(16))) char smem[kStages * kStageB];
+// Output tile staged in LDS for the row-contiguous stores: the 16-byte chunk
+// c of tile row r sits at slot so(r, c), so that the accumulator's writes (one
+// row per lane, 8 bytes each) and the row reads (16 bytes per lane) both hit 16
+// different bank groups (256 bytes = 16 slots) for 16 consecutive rows.  With
+// CR = 8 (mod 16) chunks per row, row parity picks the half and (r / 2) % 8 the
+// slot within it; with CR = 0 (mod 16), r % 16 picks the slot.  XOR with a
+// value below 8 (or 16) keeps the slot inside the row.
+template <int CR>
+__device__ __forceinline__ int so(int row, int c) {
+  static_assert(CR % 8 == 0, "rows of whole 128-byte lines");
+  return CR % 16 == 8 ? c ^ ((row >> 1) & 7) : c ^ (row & 15);
+}
+
+template <class G, bool LDS_OUT>
+__global__ void __launch_bounds__(256, G::MINW) linear_staged_kernel(LinearLaunch p, int n_tiles, int total) {
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / G::WF, wf = wave % G::WF;
   const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
   int lid = blockIdx.x;
   if ((total & 7) == 0) lid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
   const int nt = lid % n_tiles;
   const int64_t mt = lid / n_tiles;
-  const int64_t n0 = (int64_t)nt * kTileN;
-  const int64_t mw0 = mt * kSTileM;  // workgroup's first row
+  const int64_t n0 = (int64_t)nt * G::BN;
+  const int64_t mw0 = mt * G::BM;  // workgroup's first row
 
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)smem;
   // copy instruction t (this wave issues t = wave, wave + 4, ...) fills staged
   // rows 8t .. 8t+7 (x rows first, then W rows); lane i takes row 8t + i/8 and
   // the chunk whose swizzled slot is i % 8
   auto issue = [&](int stage) {
-    const int k0 = stage * kChunkK;
-    const unsigned buf = lds0 + (unsigned)((stage % kStages) * kStageB);
+    const int k0 = stage * G::kChunkK;
+    const unsigned buf = lds0 + (unsigned)((stage % G::STAGES) * G::STAGE_B);
 #pragma unroll
-    for (int u = 0; u < kDmaPerWave; ++u) {
-      const int t = wave + kWaves * u;
+    for (int u = 0; u < G::CPW; ++u) {
+      const int t = wave + 4 * u;
       const int r = 8 * t + (lane >> 3);
       const int chunk = (lane & 7) ^ ((r >> 1) & 7);
       const _Float16* src;
-      if (r < kSTileM) {
+      if (r < G::BM) {
         const int64_t m = min(mw0 + r, p.M - 1);
         src = p.x + m * p.x_ld + k0 + 8 * chunk;
       } else {
-        src = p.w + (n0 + (r - kSTileM)) * p.w_ld + k0 + 8 * chunk;
+        src = p.w + (n0 + (r - G::BM)) * p.w_ld + k0 + 8 * chunk;
       }
       dma16(buf + t * 1024, src);
     }
   };
 
-  f16v acc[2][kSJ];
+  f16v acc[G::IN][G::IM];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < G::IN; ++i)
 #pragma unroll
-    for (int j = 0; j < kSJ; ++j) acc[i][j] = (f16v){};
+    for (int j = 0; j < G::IM; ++j) acc[i][j] = (f16v){};
 
-  const int nst = p.K / kChunkK;
+  const int nst = p.K / G::kChunkK;
 #pragma unroll
-  for (int q = 0; q < kStages - 1; ++q)
+  for (int q = 0; q < G::STAGES - 1; ++q)
     if (q < nst) issue(q);
   for (int st = 0; st < nst; ++st) {
-    // chunk st has landed (the copies of the kStages-2 chunks after it may still fly)
-    if (st + kStages - 2 < nst)
-      wait_vmcnt<kDmaPerWave * (kStages - 2)>();
+    // chunk st has landed (the copies of the STAGES-2 chunks after it may still fly)
+    if (st + G::STAGES - 2 < nst)
+      wait_vmcnt<G::CPW * (G::STAGES - 2)>();
     else
       wait_vmcnt<0>();
     __syncthreads();  // ... everywhere; the buffer of chunk st-1 is free
-    if (st + kStages - 1 < nst) issue(st + kStages - 1);
-    const char* xb = smem + (st % kStages) * kStageB;
-    const char* wb = xb + kStageX;
+    if (st + G::STAGES - 1 < nst) issue(st + G::STAGES - 1);
+    const char* xb = smem + (st % G::STAGES) * G::STAGE_B;
+    const char* wb = xb + G::STAGE_X;
 #pragma unroll
-    for (int ks = 0; ks < kChunkK / 16; ++ks) {
+    for (int ks = 0; ks < G::kChunkK / 16; ++ks) {
       const int chunk = 2 * ks + h;
-      h8 a[2], b[kSJ];
+      h8 a[G::IN], b[G::IM];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int nl = 32 * i + c32;
-        a[i] = *reinterpret_cast<const h8*>(wb + nl * kRowB + 16 * swz(nl, chunk));
+      for (int i = 0; i < G::IN; ++i) {
+        const int nl = (wf * G::IN + i) * 32 + c32;
+        a[i] = *reinterpret_cast<const h8*>(wb + nl * G::kRowB + 16 * swz(nl, chunk));
       }
 #pragma unroll
-      for (int j = 0; j < kSJ; ++j) {
-        const int ml = wave * kSMW + 32 * j + c32;
-        b[j] = *reinterpret_cast<const h8*>(xb + ml * kRowB + 16 * swz(ml, chunk));
+      for (int j = 0; j < G::IM; ++j) {
+        const int ml = (wr * G::IM + j) * 32 + c32;
+        b[j] = *reinterpret_cast<const h8*>(xb + ml * G::kRowB + 16 * swz(ml, chunk));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < G::IN; ++i)
 #pragma unroll
-        for (int j = 0; j < kSJ; ++j)
+        for (int j = 0; j < G::IM; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   }
 
-  const int64_t m0 = mw0 + (int64_t)wave * kSMW;
+  // acc[i][j][4r + q]: feature (wf IN + i) 32 + 8r + 4h + q of row (wr IM + j) 32 + l%32
+  if constexpr (LDS_OUT) {
+    // y tile -> LDS (bias added, rounded to fp16), then whole 16-byte chunks of
+    // row segments -> y: a wave's store covers 64 / CR rows of BN features
+    constexpr int CR = G::BN / 8;  // 16-byte chunks per tile row
+    constexpr int RB = G::BN * 2;  // bytes per tile row
+    __syncthreads();               // every wave is done with the stage buffers
 #pragma unroll
-  for (int j = 0; j < kSJ; ++j) {
-    const int64_t m = m0 + 32 * j + c32;
-    if (m >= p.M) continue;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < G::IN; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t n = n0 + 32 * i + 8 * r + 4 * h;
+        const int c = (wf * G::IN + i) * 4 + r;
         float bq[4] = {0.f, 0.f, 0.f, 0.f};
         if (p.bias) {
-          const float4 b4 = *reinterpret_cast<const float4*>(p.bias + n);
+          const float4 b4 = *reinterpret_cast<const float4*>(p.bias + n0 + 8 * c + 4 * h);
           bq[0] = b4.x;
           bq[1] = b4.y;
           bq[2] = b4.z;
           bq[3] = b4.w;
         }
-        h4 out;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) out[q] = (_Float16)(acc[i][j][4 * r + q] + bq[q]);
-        *reinterpret_cast<h4*>(p.y + m * p.y_ld + n) = out;
+        for (int j = 0; j < G::IM; ++j) {
+          const int row = (wr * G::IM + j) * 32 + c32;
+          h4 out;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) out[q] = (_Float16)(acc[i][j][4 * r + q] + bq[q]);
+          *reinterpret_cast<h4*>(smem + row * RB + 16 * so<CR>(row, c) + 8 * h) = out;
+        }
       }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < G::BM * CR / 256; ++u) {
+      const int e = tid + 256 * u, row = e / CR, c = e % CR;
+      const int64_t m = mw0 + row;
+      if (m < p.M)
+        *reinterpret_cast<h8*>(p.y + m * p.y_ld + n0 + 8 * c) =
+            *reinterpret_cast<const h8*>(smem + row * RB + 16 * so<CR>(row, c));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < G::IM; ++j) {
+      const int64_t m = mw0 + (wr * G::IM + j) * 32 + c32;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int i = 0; i < G::IN; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t n = n0 + (wf * G::IN + i) * 32 + 8 * r + 4 * h;
+          float bq[4] = {0.f, 0.f, 0.f, 0.f};
+          if (p.bias) {
+            const float4 b4 = *reinterpret_cast<const float4*>(p.bias + n);
+            bq[0] = b4.x;
+            bq[1] = b4.y;
+            bq[2] = b4.z;
+            bq[3] = b4.w;
+          }
+          h4 out;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) out[q] = (_Float16)(acc[i][j][4 * r + q] + bq[q]);
+          *reinterpret_cast<h4*>(p.y + m * p.y_ld + n) = out;
+        }
+    }
   }
+}
+
+template <class G>
+hipError_t launch_staged(const LinearLaunch& a, hipStream_t stream) {
+  static_assert(G::BM * G::BN * 2 <= G::LDS, "the output tile fits in the stage buffers");
+  const int n_tiles = a.N / G::BN;
+  const int64_t total = ((a.M + G::BM - 1) / G::BM) * n_tiles;
+  if (total > 0x7fffffff) return hipErrorInvalidValue;
+  // 16-byte row stores need y 16-byte aligned with a row pitch of 8 elements
+  if ((reinterpret_cast<uintptr_t>(a.y) & 15) == 0 && a.y_ld % 8 == 0)
+    hipLaunchKernelGGL((linear_staged_kernel<G, true>), dim3((unsigned)total), dim3(256), 0, stream, a, n_tiles,
+                       (int)total);
+  else
+    hipLaunchKernelGGL((linear_staged_kernel<G, false>), dim3((unsigned)total), dim3(256), 0, stream, a, n_tiles,
+                       (int)total);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_linear(const LinearLaunch& a, hipStream_t stream) {
+  if (a.K % 64 == 0) {
+    // Tile shape by problem shape (measured at the projections of the four
+    // UNet levels): 256 x 256 tiles where K is long and they still give about
+    // one workgroup per CU (the contraction-bound case), 256 x 64 where M is
+    // large enough for 1024+ of them, 128 x 64 otherwise.
+    using Square = GemmCfg<2, 4, 4, 2>;
+    using Tall = GemmCfg<4, 2, 2, 2>;
+    using Base = GemmCfg<4, 1, 2, 2>;
+    auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * (a.N / bn); };
+    if (a.K >= 1024 && a.N % Square::BN == 0 && tiles(Square::BM, Square::BN) >= 224)
+      return launch_staged<Square>(a, stream);
+    if (tiles(Tall::BM, Tall::BN) >= 1024) return launch_staged<Tall>(a, stream);
+    return launch_staged<Base>(a, stream);
+  }
   const int n_tiles = a.N / kTileN;
   const int64_t m_tiles = (a.M + kTileM - 1) / kTileM;
   const int64_t total = m_tiles * n_tiles;
   if (total > 0x7fffffff) return hipErrorInvalidValue;
-  if (a.K % kChunkK == 0) {
-    const int64_t st_total = ((a.M + kSTileM - 1) / kSTileM) * n_tiles;
-    if (st_total > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(linear_staged_kernel, dim3((unsigned)st_total), dim3(64 * kWaves), 0, stream, a, n_tiles,
-                       (int)st_total);
-  } else if (a.K % (16 * kPrefetch) == 0)
+  if (a.K % (16 * kPrefetch) == 0)
     hipLaunchKernelGGL(linear_kernel<kPrefetch>, dim3((unsigned)total), dim3(64 * kWaves), 0, stream, a, n_tiles,
                        (int)total);
   else

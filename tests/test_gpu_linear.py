@@ -55,6 +55,31 @@ def test_linear_full_compare(B, name, M, N, K, bias):
     check(got.cpu().numpy(), linear(x, w, b), K)
 
 
+# Shapes that select each tile configuration of the K % 64 == 0 kernel
+# (128 x 64, 256 x 64 for large M, 256 x 256 for long K), with ragged row tails.
+TILES = [("128x64 tiles", 333, 128, 128), ("256x64 tiles", 16300, 1024, 128), ("256x256 tiles", 3600, 3840, 1024)]
+
+
+@pytest.mark.parametrize("row_stores", [True, False], ids=["row stores", "direct stores"])
+@pytest.mark.parametrize("name,M,N,K", TILES, ids=[c[0] for c in TILES])
+def test_tile_configs_sampled(B, name, M, N, K, row_stores):
+    """Every tile configuration, with bias, through both output paths: y 16-byte
+    aligned with a row pitch of 8 elements (tile staged in LDS, whole 16-byte row
+    chunks stored) and a pitch of N + 4 (8-byte stores straight from registers)."""
+    say("linear tiles", name, M, N, K, "row" if row_stores else "direct")
+    x, w, b = case(name, M, N, K, True)
+    if row_stores:
+        out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    else:
+        out = torch.empty((M, N + 4), dtype=torch.float16, device="cuda")[:, :N]
+    got = B.linear(dev(x), dev(w), dev(b), out=out)
+    torch.cuda.synchronize()
+    # rows around every 256-row tile edge near both ends, plus a random spread
+    edges = [r for t in (256, 512, (M // 256) * 256) for r in (t - 1, t) if r < M]
+    rows = np.unique(np.concatenate([np.random.default_rng(M).integers(0, M, 200), [0, M - 1], edges]))
+    check(got.cpu().numpy()[rows], linear(x[rows], w, b), K)
+
+
 @pytest.mark.parametrize("L,C", [(4096, 320), (1024, 640), (256, 1280), (64, 1280)])
 def test_fused_qkv_projection_sampled(B, L, C):
     """to_q / to_k / to_v as one [3C, C] weight over the 16 frames of a level."""
