@@ -248,25 +248,38 @@ __global__ void __launch_bounds__(256, G::MINW) linear_staged_kernel(LinearLaunc
     if (st + G::STAGES - 1 < nst) issue(st + G::STAGES - 1);
     const char* xb = smem + (st % G::STAGES) * G::STAGE_B;
     const char* wb = xb + G::STAGE_X;
+    // all operands of the chunk's 4 steps are read up front; the schedule
+    // below issues the reads of step ks + 2 right after the products of step
+    // ks, so two steps of reads overlap the matrix core instead of waiting in
+    // front of it
+    constexpr int KS = G::kChunkK / 16;
+    h8 a[KS][G::IN], b[KS][G::IM];
 #pragma unroll
-    for (int ks = 0; ks < G::kChunkK / 16; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int chunk = 2 * ks + h;
-      h8 a[G::IN], b[G::IM];
 #pragma unroll
       for (int i = 0; i < G::IN; ++i) {
         const int nl = (wf * G::IN + i) * 32 + c32;
-        a[i] = *reinterpret_cast<const h8*>(wb + nl * G::kRowB + 16 * swz(nl, chunk));
+        a[ks][i] = *reinterpret_cast<const h8*>(wb + nl * G::kRowB + 16 * swz(nl, chunk));
       }
 #pragma unroll
       for (int j = 0; j < G::IM; ++j) {
         const int ml = (wr * G::IM + j) * 32 + c32;
-        b[j] = *reinterpret_cast<const h8*>(xb + ml * G::kRowB + 16 * swz(ml, chunk));
+        b[ks][j] = *reinterpret_cast<const h8*>(xb + ml * G::kRowB + 16 * swz(ml, chunk));
       }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int i = 0; i < G::IN; ++i)
 #pragma unroll
         for (int j = 0; j < G::IM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (G::IN + G::IM), 0);  // reads of steps 0, 1
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, G::IN * G::IM, 0);  // products of step ks
+      if (ks + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, G::IN + G::IM, 0);  // reads of step ks + 2
     }
   }
 
@@ -276,20 +289,26 @@ __global__ void __launch_bounds__(256, G::MINW) linear_staged_kernel(LinearLaunc
     // row segments -> y: a wave's store covers 64 / CR rows of BN features
     constexpr int CR = G::BN / 8;  // 16-byte chunks per tile row
     constexpr int RB = G::BN * 2;  // bytes per tile row
-    __syncthreads();               // every wave is done with the stage buffers
+    // the bias of this lane's features, all loads issued before the first use
+    float4 bias4[G::IN][4];
+#pragma unroll
+    for (int i = 0; i < G::IN; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bias4[i][r] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p.bias) {
+#pragma unroll
+      for (int i = 0; i < G::IN; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          bias4[i][r] = *reinterpret_cast<const float4*>(p.bias + n0 + 8 * ((wf * G::IN + i) * 4 + r) + 4 * h);
+    }
+    __syncthreads();  // every wave is done with the stage buffers
 #pragma unroll
     for (int i = 0; i < G::IN; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int c = (wf * G::IN + i) * 4 + r;
-        float bq[4] = {0.f, 0.f, 0.f, 0.f};
-        if (p.bias) {
-          const float4 b4 = *reinterpret_cast<const float4*>(p.bias + n0 + 8 * c + 4 * h);
-          bq[0] = b4.x;
-          bq[1] = b4.y;
-          bq[2] = b4.z;
-          bq[3] = b4.w;
-        }
+        const float bq[4] = {bias4[i][r].x, bias4[i][r].y, bias4[i][r].z, bias4[i][r].w};
 #pragma unroll
         for (int j = 0; j < G::IM; ++j) {
           const int row = (wr * G::IM + j) * 32 + c32;
@@ -300,13 +319,24 @@ __global__ void __launch_bounds__(256, G::MINW) linear_staged_kernel(LinearLaunc
         }
       }
     __syncthreads();
+    // read the thread's chunks in groups of 8, then store them
+    constexpr int U = G::BM * CR / 256;
+    static_assert(U % 8 == 0 || U < 8, "store groups");
+    constexpr int UG = U < 8 ? U : 8;
 #pragma unroll
-    for (int u = 0; u < G::BM * CR / 256; ++u) {
-      const int e = tid + 256 * u, row = e / CR, c = e % CR;
-      const int64_t m = mw0 + row;
-      if (m < p.M)
-        *reinterpret_cast<h8*>(p.y + m * p.y_ld + n0 + 8 * c) =
-            *reinterpret_cast<const h8*>(smem + row * RB + 16 * so<CR>(row, c));
+    for (int u0 = 0; u0 < U; u0 += UG) {
+      h8 v[UG];
+#pragma unroll
+      for (int u = 0; u < UG; ++u) {
+        const int e = tid + 256 * (u0 + u), row = e / CR, c = e % CR;
+        v[u] = *reinterpret_cast<const h8*>(smem + row * RB + 16 * so<CR>(row, c));
+      }
+#pragma unroll
+      for (int u = 0; u < UG; ++u) {
+        const int e = tid + 256 * (u0 + u), row = e / CR, c = e % CR;
+        const int64_t m = mw0 + row;
+        if (m < p.M) *reinterpret_cast<h8*>(p.y + m * p.y_ld + n0 + 8 * c) = v[u];
+      }
     }
   } else {
 #pragma unroll
