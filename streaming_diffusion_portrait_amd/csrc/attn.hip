@@ -304,6 +304,7 @@ struct WaveState {
   f4 oacc[C::NQB][2][C::NDT];  // O^T accumulators: [query block][16-query half][16-row d tile]
   float mrun[C::NQB];          // running offset of query l%32 of each block
   float lsum[C::NQB];          // partial row sums (S layout), when not through the matrix core
+  f16v negm[C::NQB];           // -mrun in every accumulator slot: the seed of fast S^T products (no ones column)
 };
 
 // Lane constants.
@@ -325,25 +326,26 @@ __device__ __forceinline__ void load_k(const char* smem, int kblk, const LaneCtx
 
 // S^T = K Q^T for every query block of the wave, from K operands in registers.
 // (Steps outermost: consecutive products accumulate into different query
-// blocks, so none waits for the one just issued.)
-template <class C>
+// blocks, so none waits for the one just issued.)  SEED: the accumulation
+// starts from -offset instead of 0, so the scores come out with the frozen
+// offset already subtracted (fast blocks when d leaves no ones column).
+template <class C, bool SEED>
 __device__ __forceinline__ void qk_regs(const h8 (&ka)[C::KST], const WaveState<C>& ws, f16v (&sacc)[C::NQB]) {
-#pragma unroll
-  for (int qb = 0; qb < C::NQB; ++qb) sacc[qb] = (f16v){};
 #pragma unroll
   for (int st = 0; st < C::KST; ++st)
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb)
-      sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[st], ws.qf[qb][st], sacc[qb], 0, 0, 0);
+      sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[st], ws.qf[qb][st],
+                                                        st > 0 ? sacc[qb] : SEED ? ws.negm[qb] : (f16v){}, 0, 0, 0);
 }
 
 // S^T(block) = K(block) Q^T for every query block of the wave.
-template <class C>
+template <class C, bool SEED>
 __device__ __forceinline__ void qk_block(const char* smem, int kblk, const WaveState<C>& ws, const LaneCtx& lc,
                                          f16v (&sacc)[C::NQB]) {
   h8 ka[C::KST];
   load_k<C>(smem, kblk, lc, ka);
-  qk_regs<C>(ka, ws, sacc);
+  qk_regs<C, SEED>(ka, ws, sacc);
 }
 
 // V^T operands of one 32-key block.
@@ -424,7 +426,7 @@ __device__ __forceinline__ void softmax_block(f16v (&sacc)[C::NQB], WaveState<C>
       }
     }
   }
-  if (EXACT || !C::ONES) {
+  if (EXACT) {  // fast blocks carry the frozen offset inside the scores already
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
@@ -483,7 +485,7 @@ __device__ __forceinline__ void tile_step(const char* smem, int kt, int valid, b
   for (int kb = 0; kb < C::NKB; ++kb) {
     if (kb > 0 && valid <= 32 * kb) break;  // a tile's last block holds no key (short segments)
     f16v s[C::NQB];
-    qk_block<C>(smem, kt + kb * C::KBLK, ws, lc, s);
+    qk_block<C, FAST && !C::ONES>(smem, kt + kb * C::KBLK, ws, lc, s);
     h8 va[C::NDT];
     load_vt<C>(smem, kt + C::TILEB + kb * C::KBLK, lc, va);
     h8 pb[C::NQB][2];
@@ -626,7 +628,7 @@ __device__ __forceinline__ void pipe_iteration(const char* smem, int vblk, int k
   bool resc;
   h8 va[C::NDT];
   load_vt<C>(smem, vblk, lc, va);
-  if (QK) qk_regs<C>(ka_cur, ws, s_out);
+  if (QK) qk_regs<C, !C::ONES>(ka_cur, ws, s_out);  // pipelined blocks are fast
   if (SM) softmax_block<C, false>(s_in, ws, lc, 32, false, p_out, alpha, resc);
   if (KR) load_k<C>(smem, kblk3, lc, ka_next);  // after the products read ka_cur
   pv_block<C>(va, p_in, ws);
@@ -780,6 +782,11 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
 #pragma unroll
           for (int qb = 0; qb < C::NQB; ++qb) ws.qf[qb][C::KST - 1][0] = (_Float16)(-ws.mrun[qb]);  // offset joins the product
         }
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ws.negm[qb][r] = -ws.mrun[qb];  // offset seeds the product
       }
       fast = ok;
     }
@@ -807,9 +814,9 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
       {
         float alpha[C::NQB];
         bool resc;
-        qk_block<C>(smem, kblk(0), ws, lc, sA);
+        qk_block<C, !C::ONES>(smem, kblk(0), ws, lc, sA);
         softmax_block<C, false>(sA, ws, lc, 32, false, pA, alpha, resc);
-        qk_block<C>(smem, kblk(1), ws, lc, sB);
+        qk_block<C, !C::ONES>(smem, kblk(1), ws, lc, sB);
         if (2 < nb) load_k<C>(smem, kblk(2), lc, kaA);
       }
       // steady state: the copies of the NBUF-4 tiles after u+3 may stay in
