@@ -1110,7 +1110,7 @@ hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream) {
     case 32: return launch_cfg<32, 2, 2, 4, 2, true, 4>(p, stream);
     case 40: return launch_cfg<40, 2, 2, 4, 2, true, 4>(p, stream);
     case 80: return launch_cfg<80, 1, 2, 4, 1, true, 8>(p, stream);
-    case 160: return launch_cfg<160, 1, 2, 2, 1, false, 4>(p, stream);
+    case 160: return launch_cfg<160, 1, 2, 3, 1, false, 4>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
