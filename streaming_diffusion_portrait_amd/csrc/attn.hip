@@ -525,14 +525,21 @@ __device__ __forceinline__ void sched_iteration() {
 // The softmax of one fast block (offset already inside the scores) as a
 // stream of single vector instructions, so that a schedule can place each of
 // them: per query block, 16 exponentials, 8 packs to fp16 (each issued two
-// exponentials after its inputs, so it never waits for them) and 4 permlane16
-// swaps that assemble P^T.  kSmOps instructions per query block.
-constexpr int kSmOps = 28;
+// exponentials after its inputs, so it never waits for them), 4 permlane16
+// swaps that assemble P^T and, without a ones row in V^T, 8 dot products that
+// add the packed probabilities to the row sums.  sm_ops<C>() instructions per
+// query block.
+template <class C>
+constexpr int sm_ops() {
+  return C::ONES ? 28 : 36;
+}
 template <class C>
 struct FastSoftmax {
+  static constexpr int kSmOps = sm_ops<C>();
   f16v* s;          // [NQB] scores -> exponentials, in place
   unsigned pk[C::NQB][8];
   h8* pb;           // [NQB][2] P^T operands out
+  float* lsum;      // [NQB] row sums (no ones row)
   __device__ __forceinline__ void op(int v) {
     const int qb = v / kSmOps, r = v % kSmOps;
     if (r < 4) {  // exponentials 0..3
@@ -544,6 +551,9 @@ struct FastSoftmax {
     } else if (r < 24) {  // packs 6, 7
       const int i = r - 16;
       pk[qb][i] = pack_h2(s[qb][2 * i], s[qb][2 * i + 1]);
+    } else if (r >= 28) {  // row sums
+      const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+      lsum[qb] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pk[qb][r - 28]), one2, lsum[qb], false);
     } else {  // swaps: pack (2j+x) with pack (2j+2+x) for j = 0, 2 and x = 0, 1
       const int k = r - 24, x = k & 1, j = (k >> 1) * 4;
       const auto sw = __builtin_amdgcn_permlane16_swap(pk[qb][j + x], pk[qb][j + 2 + x], false, false);
@@ -577,9 +587,12 @@ __device__ __forceinline__ void pipe_iteration_fixed(const char* smem, int vblk,
                                                      f16v (&s_out)[C::NQB], const h8 (&p_in)[C::NQB][2],
                                                      h8 (&p_out)[C::NQB][2], const h8 (&ka_cur)[C::KST],
                                                      h8 (&ka_next)[C::KST], WaveState<C>& ws, const LaneCtx& lc) {
-  static_assert(C::ONES, "the fast softmax stream needs the offset inside the scores");
   constexpr int NQK = C::KST * C::NQB, NPV = C::NDT * C::NQB * 2, NM = NQK + NPV;
-  constexpr int NV = kSmOps * C::NQB;
+  constexpr int NV = sm_ops<C>() * C::NQB;
+  // vector instructions after each S^T / PV product (d = 40: tuned; otherwise
+  // 4 after each S^T product and the rest spread over the PV products)
+  constexpr int SQK = C::ONES ? PL_SLOT_QK : 4;
+  constexpr int SPV = C::ONES ? PL_SLOT_PV : (NV - NQK * SQK + NPV - 1) / NPV;
   h8 va[C::NDT];
   load_vt<C>(smem, vblk, lc, va);
   load_k<C>(smem, kblk3, lc, ka_next);
@@ -587,18 +600,25 @@ __device__ __forceinline__ void pipe_iteration_fixed(const char* smem, int vblk,
   FastSoftmax<C> sm;
   sm.s = s_in;
   sm.pb = &p_out[0][0];
+  sm.lsum = ws.lsum;
   int v = 0;
+  // Two waves share each SIMD.  The wave in its PV phase (16x16 products, the
+  // packs and swaps) runs at raised issue priority, so while one wave streams
+  // its PV products the other fills the gaps with its S^T products and
+  // exponentials, and the two drift into alternating phases.
+  __builtin_amdgcn_s_setprio(0);
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
+    if (m == NQK) __builtin_amdgcn_s_setprio(1);
     if (m < NQK) {  // S^T(b+2): steps outermost, query blocks alternate
       const int st = m / C::NQB, qb = m % C::NQB;
-      s_out[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka_cur[st], ws.qf[qb][st], st == 0 ? (f16v){} : s_out[qb],
-                                                          0, 0, 0);
+      s_out[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+          ka_cur[st], ws.qf[qb][st], st > 0 ? s_out[qb] : C::ONES ? (f16v){} : ws.negm[qb], 0, 0, 0);
     } else {  // O^T += V^T(b) P^T(b): d tiles outermost (the V reads land in that order)
       const int i = m - NQK, t = i / (2 * C::NQB), qb = (i / 2) % C::NQB, grp = i % 2;
       ws.oacc[qb][grp][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t], p_in[qb][grp], ws.oacc[qb][grp][t], 0, 0, 0);
     }
-    const int nv = m < NQK ? PL_SLOT_QK : PL_SLOT_PV;
+    const int nv = m < NQK ? SQK : SPV;
 #pragma unroll
     for (int k = 0; k < nv; ++k)
       if (v + k < NV) sm.op(v + k);
@@ -636,18 +656,16 @@ __device__ __forceinline__ void pipe_iteration(const char* smem, int vblk, int k
   __builtin_amdgcn_sched_barrier(0);  // iterations do not mix: each keeps its own interleave
 }
 
-// A full pipelined iteration: the fixed-order form where the offset rides in
-// the scores (d = 40), else the compiler-scheduled one.
+// A full pipelined iteration: the fixed-order form (the compiler-scheduled one
+// when PL_FIXED_ORDER is 0).
 template <class C>
 __device__ __forceinline__ void pipe_steady(const char* smem, int vblk, int kblk3, f16v (&s_in)[C::NQB],
                                             f16v (&s_out)[C::NQB], const h8 (&p_in)[C::NQB][2],
                                             h8 (&p_out)[C::NQB][2], const h8 (&ka_cur)[C::KST], h8 (&ka_next)[C::KST],
                                             WaveState<C>& ws, const LaneCtx& lc) {
 #if PL_FIXED_ORDER
-  if constexpr (C::ONES) {
-    pipe_iteration_fixed<C>(smem, vblk, kblk3, s_in, s_out, p_in, p_out, ka_cur, ka_next, ws, lc);
-    return;
-  }
+  pipe_iteration_fixed<C>(smem, vblk, kblk3, s_in, s_out, p_in, p_out, ka_cur, ka_next, ws, lc);
+  return;
 #endif
   pipe_iteration<C, true, true, true>(smem, vblk, kblk3, s_in, s_out, p_in, p_out, ka_cur, ka_next, ws, lc);
 }
@@ -836,6 +854,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
         if (cp.issued < ntiles && cp.issued < u + 1 + C::NBUF) fast_issue<C>(p, smem, fc, cp, f, hd, wave, lc.lane);
         pipe_steady<C>(smem, vblk(2 * u + 1), kblk(2 * u + 4), sA, sB, pB, pA, kaB, kaA, ws, lc);
       }
+      __builtin_amdgcn_s_setprio(0);  // back to the default for the tail
       // Blocks 2u.. are left: four of them (every tile they need has landed
       // and no copy remains), or two when the sequence has only two tiles.
       if (nb - 2 * u == 4) {
