@@ -275,7 +275,14 @@ __device__ __forceinline__ void fast_seek(const KParams& p, FastCopier<C>& fc, i
   fc.vp = uniform_ptr(reinterpret_cast<const char*>(sg.v + base));
   fc.step = uniform64(sg.ld * 2 * C::BN);
   fc.rem = __builtin_amdgcn_readfirstlane((int)((sg.len - off) / C::BN));
-  fc.voff = (unsigned)lane * (unsigned)(sg.ld * 2);
+  // the lane id is recomputed here rather than kept live across the pipeline
+  // (a spilled copy would be reloaded, and that load's wait would also wait
+  // for every copy in flight)
+  // (volatile, so that it is not hoisted out of the loop either)
+  (void)lane;
+  unsigned ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  fc.voff = ln * (unsigned)(sg.ld * 2);
 }
 
 template <class C>
