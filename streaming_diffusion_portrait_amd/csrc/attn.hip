@@ -974,10 +974,28 @@ __device__ __forceinline__ void load_q_block(const KParams& p, const _Float16* q
 #define PL_SHORT_WGS 1024  // workgroups a short-context launch aims for (4 per CU)
 #endif
 
+// Q and O pass through LDS: each wave stages its 32-row block of Q (the head's
+// d columns of 32 rows) with direct-to-LDS copies in which D/8 consecutive
+// lanes read one row's 2d contiguous bytes, and writes O back the same way
+// from LDS, so every memory instruction moves whole row slices instead of the
+// 16- and 8-byte pieces of the matrix-core layouts.  Two such buffers per wave:
+// the next block's Q lands while the current one is computed; O overwrites the
+// Q it was computed from.
+template <class C>
+struct ShortStage {
+  static constexpr int QB = 32 * C::D * 2;      // bytes of one 32-row block (row pitch 2d)
+  static constexpr int CPRQ = C::D / 8;         // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPRQ;         // rows per wave-wide copy
+  static constexpr int NQI = (32 + RPI - 1) / RPI;  // copies per block
+  static constexpr int LDS = C::BUFB + C::W * 2 * QB;  // one K/V tile pair + the waves' buffers
+  static_assert(NQI <= 24, "vmcnt wait table range");
+};
+
 template <class C>
 __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams p, int nsplit) {
   static_assert(C::NQB == 1, "one 32-query block per step");
-  __shared__ __attribute__((aligned(16))) char smem[C::LDSB];
+  using S = ShortStage<C>;
+  __shared__ __attribute__((aligned(16))) char smem[S::LDS];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1000,8 +1018,8 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
   const int f = fs / nsplit;
   const int split = fs - f * nsplit;
 
-  if (C::ONES) {
-    for (int i = tid >> 6; i < 2 * C::NBUF; i += C::W) {
+  if (C::ONES) {  // the constant plane of the one K tile and the one V tile
+    for (int i = tid >> 6; i < 2; i += C::W) {
       h8 one = {0, 0, 0, 0, 0, 0, 0, 0};
       one[0] = (_Float16)1.0f;
       *reinterpret_cast<h8*>(smem + i * C::TILEB + C::CPR * C::PLB + 16 * lc.lane) = one;
@@ -1025,20 +1043,46 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
   const _Float16* qb_ = p.q + (int64_t)f * p.q_fs + (int64_t)hd * C::D;
   _Float16* ob = p.o + (int64_t)f * p.o_fs + (int64_t)hd * C::D;
   const int step = nsplit * C::W;
+  char* qs = smem + C::BUFB + wave * 2 * S::QB;  // this wave's two block buffers
+  const int qrow = lc.lane / S::CPRQ, qchunk = lc.lane % S::CPRQ;
+  // copy Q rows 32 blk .. 32 blk + 31 into buffer b (rows past Lq re-read the
+  // last row: their results are never stored)
+  auto q_issue = [&](int blk, int b) {
+    const char* src = reinterpret_cast<const char*>(qb_ + (int64_t)(32 * blk) * p.q_ld);
+    const unsigned dst = lds_addr(qs + b * S::QB);
+    const int last = p.Lq - 1 - 32 * blk;
+#pragma unroll
+    for (int j = 0; j < S::NQI; ++j) {
+      const int r = j * S::RPI + qrow;
+      if (lc.lane < S::RPI * S::CPRQ && r < 32)
+        lds_dma16(dst + j * S::RPI * S::CPRQ * 16, (unsigned)(min(r, last) * p.q_ld * 2 + 16 * qchunk), src);
+    }
+  };
+
   int blk = split * C::W + wave;
-  h8 qn[C::KST];
-  if (blk < nblk) load_q_block<C>(p, qb_, 32 * blk + c32, lc, qn);
+  if (blk < nblk) q_issue(blk, 0);
   wait_vm(0);
-  __syncthreads();  // the tile (and the constant plane) is in LDS
+  __syncthreads();  // the K/V tile (and the constant plane) and the first Q block are in LDS
 
   WaveState<C> ws;
-  for (; blk < nblk; blk += step) {
+  for (int b = 0; blk < nblk; blk += step, b ^= 1) {
+    const bool next = blk + step < nblk;
+    if (next) q_issue(blk + step, b ^ 1);  // that buffer's O was read out in the previous block
+    // Q of this block has landed (loads complete in order; what may still be
+    // outstanding is the previous block's stores and the copies just issued)
+    if (next)
+      wait_vm(S::NQI);
+    else
+      wait_vm(0);
+    char* buf = qs + b * S::QB;
 #pragma unroll
     for (int st = 0; st < C::KST; ++st) {
+      const int col = 16 * st + 8 * lc.h;
+      h8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (col < C::D) x = *reinterpret_cast<const h8*>(buf + c32 * (2 * C::D) + 2 * col);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ws.qf[0][st][e] = (_Float16)((float)qn[st][e] * p.c2);
+      for (int e = 0; e < 8; ++e) ws.qf[0][st][e] = (_Float16)((float)x[e] * p.c2);
     }
-    if (blk + step < nblk) load_q_block<C>(p, qb_, 32 * (blk + step) + c32, lc, qn);  // next block, in flight
     ws.mrun[0] = 0.f;
     ws.lsum[0] = 0.f;
 #pragma unroll
@@ -1047,7 +1091,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
       for (int t = 0; t < C::NDT; ++t) ws.oacc[0][grp][t] = (f4){0.f, 0.f, 0.f, 0.f};
     tile_step<C, false>(smem, 0, valid, true, ws, lc);
 
-    // normalise and write O (fp16, round to nearest even)
+    // normalise, round to fp16 (nearest even) into the block buffer
     float tot = 0.f;
     if (!C::ONES) tot = ws.lsum[0] + __shfl_xor(ws.lsum[0], 32, 64);
 #pragma unroll
@@ -1060,19 +1104,25 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
         l = __shfl(tot, 16 * grp + lc.c16, 64);
       }
       const float inv = 1.0f / l;
-      const int row = 32 * blk + 16 * grp + lc.c16;
-      if (row < p.Lq) {
+      const int row = 16 * grp + lc.c16;
 #pragma unroll
-        for (int t = 0; t < C::NDT; ++t) {
-          const int col = 16 * t + 4 * lc.g;
-          if (col < C::D) {
-            h4 out;
+      for (int t = 0; t < C::NDT; ++t) {
+        const int col = 16 * t + 4 * lc.g;
+        if (col < C::D) {
+          h4 out;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) out[r] = (_Float16)(ws.oacc[0][grp][t][r] * inv);
-            *reinterpret_cast<h4*>(ob + (int64_t)row * p.o_ld + col) = out;
-          }
+          for (int r = 0; r < 4; ++r) out[r] = (_Float16)(ws.oacc[0][grp][t][r] * inv);
+          *reinterpret_cast<h4*>(buf + row * (2 * C::D) + 2 * col) = out;
         }
       }
+    }
+    // O rows out, whole row slices per lane group
+#pragma unroll
+    for (int j = 0; j < S::NQI; ++j) {
+      const int r = j * S::RPI + qrow;
+      if (lc.lane < S::RPI * S::CPRQ && r < 32 && 32 * blk + r < p.Lq)
+        *reinterpret_cast<h8*>(ob + (int64_t)(32 * blk + r) * p.o_ld + 8 * qchunk) =
+            *reinterpret_cast<const h8*>(buf + r * (2 * C::D) + 16 * qchunk);
     }
   }
 }
@@ -1081,6 +1131,8 @@ template <int D, int MINB>
 hipError_t launch_short(const KParams& kp, hipStream_t stream) {
   using C = Cfg<D, 1, 2, 2, MINB, false, 4>;
   KParams p = kp;
+  // 32-bit per-lane copy offsets: a key tile and a 32-row Q block
+  if (p.seg[0].ld * 2 * C::BN > 0x7fffffffLL || p.q_ld * 2 * 32 > 0x7fffffffLL) return hipErrorInvalidValue;
   const int64_t base = (int64_t)p.F * p.H;
   // about four workgroups per CU in total, each wave walking one or more blocks
   const int nblk = (p.Lq + 31) / 32;
