@@ -32,14 +32,20 @@ motion_min_l2_kernel(const float* __restrict__ query, const float* __restrict__ 
   float part[PL_MAX_MOTION_BANK];
 #pragma unroll
   for (int j = 0; j < PL_MAX_MOTION_BANK; ++j) part[j] = 0.f;
+  // Every entry slot is read without a branch (slots past n re-read the last
+  // entry; their sums are ignored) and the loop is unrolled, so the loads of 8
+  // strides (all of a 512-d embedding) are in flight together instead of one
+  // memory round trip per load.
+  const float* brow[PL_MAX_MOTION_BANK];
+#pragma unroll
+  for (int j = 0; j < PL_MAX_MOTION_BANK; ++j) brow[j] = bank + (int64_t)min(j, n - 1) * D;
+#pragma unroll 8
   for (int k = lane; k < D; k += kWave) {
     const float qv = q[k];
 #pragma unroll
     for (int j = 0; j < PL_MAX_MOTION_BANK; ++j) {
-      if (j < n) {
-        const float diff = qv - bank[(int64_t)j * D + k];
-        part[j] = fmaf(diff, diff, part[j]);
-      }
+      const float diff = qv - brow[j][k];
+      part[j] = fmaf(diff, diff, part[j]);
     }
   }
   float best = 0.f;
