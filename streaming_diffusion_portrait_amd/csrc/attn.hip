@@ -39,9 +39,11 @@
 // evaluates softmax(b+1) on the vector ALU, O^T += V^T(b) P^T(b) and
 // S^T(b+2) = K(b+2) Q^T on the matrix core, and reads the K operands of
 // block b+3 and V of block b from LDS -- independent streams that are
-// interleaved instruction by instruction, so the exponentials and
-// conversions issue while the matrix products execute and no product waits
-// for an LDS read issued in the same iteration except PV(b) for V(b).
+// interleaved instruction by instruction in a fixed order, so the
+// exponentials and conversions issue while the matrix products execute and
+// no product waits for an LDS read issued in the same iteration except PV(b)
+// for V(b).  Two waves share each SIMD; the one in its PV part runs at raised
+// issue priority, which settles the pair into alternating phases.
 //
 // Softmax (fp32, log2 units).  Q is pre-scaled by scale*log2(e) and rounded
 // to fp16 once, so the matrix core yields s = scale*log2(e)*q.k directly.
@@ -53,10 +55,11 @@
 //     taken.  For a head dim that leaves a zero-padded column (d = 40), the
 //     padding carries the offset into the matrix core: K gets a column of
 //     ones and Q the value -m, so s - m comes out of the MFMA and p = exp2 of
-//     the accumulator.  A frozen offset only fails if a later score exceeds
-//     it by 16 or more (p beyond the fp16 range): a row sum then turns
-//     inf/NaN, which is checked once at the end; the workgroup then
-//     recomputes everything with exact tiles.
+//     the accumulator; for the other head dims the S^T products start from an
+//     accumulator seeded with -m, to the same effect.  A frozen offset only
+//     fails if a later score exceeds it by 16 or more (p beyond the fp16
+//     range): a row sum then turns inf/NaN, which is checked once at the end;
+//     the workgroup then recomputes everything with exact tiles.
 //   * Row sums come from the same fp16 values that weight V: through the
 //     matrix core (a row of ones in the V^T padding, d = 40) or with
 //     v_dot2_f32_f16 on the packed probabilities (other head dims).
