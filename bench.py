@@ -73,7 +73,7 @@ def traffic_record(kernel_key):
     source has changed since, the figure no longer applies and None is
     returned.
     """
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", "refbank_attn_full_round_m3_hbm_traffic.md")
     src = os.path.join(ROOT, "streaming_diffusion_portrait_amd", "csrc", "attn.hip")
     if not (os.path.exists(path) and os.path.exists(src)):
         return None
