@@ -60,6 +60,16 @@ SMALL = [
     ("d32 NT4", 32, 1, 1024, 2, [(1024, False), (1024, True)], 1.0),
     ("single key", 40, 2, 64, 2, [(1, False)], 1.0),
     ("bank only", 80, 3, 50, 1, [(77, True)], 1.0),
+    # the most segments a call takes (8), per-frame and shared mixed: ragged ones
+    # (tile-by-tile path) and whole tiles only (the pipelined path seeks across them)
+    ("d40 eight ragged segments", 40, 2, 150, 2,
+     [(150, False), (64, True), (1, True), (65, False), (128, True), (3, True), (64, False), (100, True)], 1.0),
+    ("d40 eight whole segments", 40, 2, 128, 2,
+     [(128, False), (64, True), (192, True), (64, False), (128, True), (64, True), (64, False), (256, True)], 1.0),
+    ("d80 eight whole segments", 80, 2, 256, 1,
+     [(256, False), (64, True), (128, True), (64, False), (64, True), (192, True), (64, False), (64, True)], 1.0),
+    ("d160 eight ragged segments", 160, 2, 70, 1,
+     [(70, False), (30, True), (64, True), (64, False), (1, True), (129, True), (7, False), (64, True)], 1.0),
 ]
 
 
