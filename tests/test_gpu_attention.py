@@ -59,6 +59,8 @@ SMALL = [
     ("d32 ragged", 32, 2, 257, 2, [(257, False), (256, True), (5, True)], 1.0),
     ("d32 NT4", 32, 1, 1024, 2, [(1024, False), (1024, True)], 1.0),
     ("single key", 40, 2, 64, 2, [(1, False)], 1.0),
+    ("one query row", 40, 2, 1, 2, [(1, False), (130, True)], 1.0),
+    ("one query row, whole tiles", 80, 2, 1, 1, [(64, False), (128, True)], 1.0),
     ("bank only", 80, 3, 50, 1, [(77, True)], 1.0),
     # the most segments a call takes (8), per-frame and shared mixed: ragged ones
     # (tile-by-tile path) and whole tiles only (the pipelined path seeks across them)
@@ -258,6 +260,9 @@ SHORT = [
     ("clip d40 small", 40, 2, 100, 2, 1, True),
     ("ctx 64 d40", 40, 2, 1000, 1, 64, True),
     ("ctx 50 d80 ragged rows", 80, 1, 37, 2, 50, False),
+    ("one query row d40", 40, 3, 1, 2, 32, False),
+    ("one query row d160 clip", 160, 1, 1, 1, 1, True),
+    ("expr d40 8 heads, 33 rows", 40, 2, 33, 8, 32, False),
 ]
 
 
