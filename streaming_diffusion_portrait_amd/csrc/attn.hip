@@ -117,6 +117,9 @@ struct Cfg {
   static constexpr int KST = (D + 15) / 16;   // 16-wide contraction steps of S^T
   static constexpr int NDT = (D + 15) / 16;   // 16-row tiles of O^T
   static constexpr bool ONES = (D % 16) != 0; // padding column D carries ones / -m
+  // no ones column (pipelined d = 32, 80): the row sums come from two more PV
+  // products per query block with a constant A whose first row is ones
+  static constexpr bool RSUM = !ONES && PIPE_;
   static constexpr int CPR = D / 8;           // 16-byte chunks per key row (dims 8c..8c+7)
   static constexpr int NPL = 2 * KST;         // planes per tile: the chunks, then the (1, 0, ..., 0) plane if any
   static constexpr int PLB = 64 * 16 + PL_PLANE_PAD;  // bytes per plane (64 keys x 16 bytes + padding)
@@ -315,6 +318,8 @@ struct WaveState {
   float mrun[C::NQB];          // running offset of query l%32 of each block
   float lsum[C::NQB];          // partial row sums (S layout), when not through the matrix core
   f16v negm[C::NQB];           // -mrun in every accumulator slot: the seed of fast S^T products (no ones column)
+  f4 osum[C::NQB][2];          // RSUM: row 0 holds the row sums of the half's 16 queries
+  h8 onesA;                    // RSUM: the constant A (row 0 ones: lanes with l % 16 == 0)
 };
 
 // Lane constants.
@@ -386,6 +391,13 @@ __device__ __forceinline__ void pv_block(const h8 (&va)[C::NDT], const h8 (&pb)[
 #pragma unroll
       for (int grp = 0; grp < 2; ++grp)
         ws.oacc[qb][grp][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t], pb[qb][grp], ws.oacc[qb][grp][t], 0, 0, 0);
+  if constexpr (C::RSUM) {
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb)
+#pragma unroll
+      for (int grp = 0; grp < 2; ++grp)
+        ws.osum[qb][grp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ws.onesA, pb[qb][grp], ws.osum[qb][grp], 0, 0, 0);
+  }
 }
 
 // Softmax of one 32-key block: S^T -> P^T operands; keys at or beyond
@@ -432,7 +444,7 @@ __device__ __forceinline__ void softmax_block(f16v (&sacc)[C::NQB], WaveState<C>
         const float mnew = fmaxf(ws.mrun[qb], mx[qb]);
         alpha[qb] = __builtin_amdgcn_exp2f(ws.mrun[qb] - mnew);
         ws.mrun[qb] = mnew;
-        ws.lsum[qb] *= alpha[qb];
+        if (!C::RSUM) ws.lsum[qb] *= alpha[qb];
       }
     }
   }
@@ -451,7 +463,7 @@ __device__ __forceinline__ void softmax_block(f16v (&sacc)[C::NQB], WaveState<C>
       for (int x = 0; x < 2; ++x)
         pk[i][x] = pack_h2(__builtin_amdgcn_exp2f(sacc[qb][4 * i + 2 * x]),
                            __builtin_amdgcn_exp2f(sacc[qb][4 * i + 2 * x + 1]));
-    if (!C::ONES) {
+    if (!C::ONES && !C::RSUM) {
       const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -484,6 +496,7 @@ __device__ __forceinline__ void rescale_acc(WaveState<C>& ws, const LaneCtx& lc,
       const float a = __shfl(alpha[qb], 16 * grp + lc.c16, 64);
 #pragma unroll
       for (int t = 0; t < C::NDT; ++t) ws.oacc[qb][grp][t] *= a;
+      if constexpr (C::RSUM) ws.osum[qb][grp] *= a;
     }
 }
 
@@ -541,7 +554,7 @@ __device__ __forceinline__ void sched_iteration() {
 // query block.
 template <class C>
 constexpr int sm_ops() {
-  return C::ONES ? 28 : 36;
+  return (C::ONES || C::RSUM) ? 28 : 36;
 }
 template <class C>
 struct FastSoftmax {
@@ -597,7 +610,7 @@ __device__ __forceinline__ void pipe_iteration_fixed(const char* smem, int vblk,
                                                      f16v (&s_out)[C::NQB], const h8 (&p_in)[C::NQB][2],
                                                      h8 (&p_out)[C::NQB][2], const h8 (&ka_cur)[C::KST],
                                                      h8 (&ka_next)[C::KST], WaveState<C>& ws, const LaneCtx& lc) {
-  constexpr int NQK = C::KST * C::NQB, NPV = C::NDT * C::NQB * 2, NM = NQK + NPV;
+  constexpr int NQK = C::KST * C::NQB, NPV = (C::NDT + (C::RSUM ? 1 : 0)) * C::NQB * 2, NM = NQK + NPV;
   constexpr int NV = sm_ops<C>() * C::NQB;
   // vector instructions after each S^T / PV product (d = 40: tuned; otherwise
   // 4 after each S^T product and the rest spread over the PV products)
@@ -624,9 +637,12 @@ __device__ __forceinline__ void pipe_iteration_fixed(const char* smem, int vblk,
       const int st = m / C::NQB, qb = m % C::NQB;
       s_out[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
           ka_cur[st], ws.qf[qb][st], st > 0 ? s_out[qb] : C::ONES ? (f16v){} : ws.negm[qb], 0, 0, 0);
-    } else {  // O^T += V^T(b) P^T(b): d tiles outermost (the V reads land in that order)
+    } else {  // O^T += V^T(b) P^T(b): d tiles outermost (the V reads land in that order), then the row sums
       const int i = m - NQK, t = i / (2 * C::NQB), qb = (i / 2) % C::NQB, grp = i % 2;
-      ws.oacc[qb][grp][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t], p_in[qb][grp], ws.oacc[qb][grp][t], 0, 0, 0);
+      if (t < C::NDT)
+        ws.oacc[qb][grp][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t], p_in[qb][grp], ws.oacc[qb][grp][t], 0, 0, 0);
+      else
+        ws.osum[qb][grp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ws.onesA, p_in[qb][grp], ws.osum[qb][grp], 0, 0, 0);
     }
     const int nv = m < NQK ? SQK : SPV;
 #pragma unroll
@@ -739,6 +755,10 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
   // K step st: lane half h reads plane 2st+h at key c32.  V^T read r of lane
   // (g, c16): key vrow(g) + 16r + c16/4, dims 4(c16%4)..+3 of the 16-dim tile,
   // i.e. plane 2t + (c16%4)/2, byte 8*(c16%2) of the key's chunk.
+  if (C::RSUM) {  // A of the row-sum products: row 0 (lanes with l % 16 == 0) all ones
+    const _Float16 a1 = lc.c16 == 0 ? (_Float16)1.0f : (_Float16)0.0f;
+    ws.onesA = (h8){a1, a1, a1, a1, a1, a1, a1, a1};
+  }
   lc.krow_off = c32 * 16 + lc.h * C::PLB;
 #pragma unroll
   for (int r = 0; r < 2; ++r)
@@ -782,6 +802,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
       for (int grp = 0; grp < 2; ++grp)
 #pragma unroll
         for (int t = 0; t < C::NDT; ++t) ws.oacc[qb][grp][t] = (f4){0.f, 0.f, 0.f, 0.f};
+      if (C::RSUM) ws.osum[qb][0] = ws.osum[qb][1] = (f4){0.f, 0.f, 0.f, 0.f};
       if (C::ONES && lc.h) ws.qf[qb][C::KST - 1][0] = (_Float16)0.0f;  // offset column: none yet
     }
 
@@ -903,6 +924,8 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
 #pragma unroll
           for (int grp = 0; grp < 2; ++grp) bad |= !(fabsf(ws.oacc[qb][grp][tl][rl]) <= 3.0e38f);
         }
+      } else if (C::RSUM) {
+        if (lc.g == 0) bad |= !(fabsf(ws.osum[qb][0][0]) <= 3.0e38f) || !(fabsf(ws.osum[qb][1][0]) <= 3.0e38f);
       } else {
         bad |= !(fabsf(ws.lsum[qb]) <= 3.0e38f);
       }
@@ -923,13 +946,15 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
 #pragma unroll
   for (int qb = 0; qb < C::NQB; ++qb) {
     float tot = 0.f;
-    if (!C::ONES) tot = ws.lsum[qb] + __shfl_xor(ws.lsum[qb], 32, 64);
+    if (!C::ONES && !C::RSUM) tot = ws.lsum[qb] + __shfl_xor(ws.lsum[qb], 32, 64);
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp) {
       float l;
       if (C::ONES) {
         constexpr int tl = C::D / 16, gl = (C::D % 16) / 4, rl = C::D % 4;
         l = __shfl(ws.oacc[qb][grp][tl][rl], 16 * gl + lc.c16, 64);
+      } else if (C::RSUM) {
+        l = __shfl(ws.osum[qb][grp][0], lc.c16, 64);  // row 0: lanes 0..15
       } else {
         l = __shfl(tot, 16 * grp + lc.c16, 64);
       }
