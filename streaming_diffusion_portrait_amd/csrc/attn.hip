@@ -60,9 +60,10 @@
 //     fails if a later score exceeds it by 16 or more (p beyond the fp16
 //     range): a row sum then turns inf/NaN, which is checked once at the end;
 //     the workgroup then recomputes everything with exact tiles.
-//   * Row sums come from the same fp16 values that weight V: through the
-//     matrix core (a row of ones in the V^T padding, d = 40) or with
-//     v_dot2_f32_f16 on the packed probabilities (other head dims).
+//   * Row sums come from the same fp16 values that weight V, through the
+//     matrix core: a row of ones in the V^T padding (d = 40), or two more PV
+//     products per query block whose A is a constant with a first row of ones
+//     (other head dims).
 #include "pl_internal.h"
 
 #include <algorithm>
@@ -117,9 +118,10 @@ struct Cfg {
   static constexpr int KST = (D + 15) / 16;   // 16-wide contraction steps of S^T
   static constexpr int NDT = (D + 15) / 16;   // 16-row tiles of O^T
   static constexpr bool ONES = (D % 16) != 0; // padding column D carries ones / -m
-  // no ones column (pipelined d = 32, 80): the row sums come from two more PV
-  // products per query block with a constant A whose first row is ones
-  static constexpr bool RSUM = !ONES && PIPE_;
+  // no ones column (d = 32, 80, 160): the row sums come from two more PV
+  // products per query block with a constant A whose first row is ones (with
+  // a ones column, from the ones row of the V^T padding)
+  static constexpr bool RSUM = !ONES;
   static constexpr int CPR = D / 8;           // 16-byte chunks per key row (dims 8c..8c+7)
   static constexpr int NPL = 2 * KST;         // planes per tile: the chunks, then the (1, 0, ..., 0) plane if any
   static constexpr int PLB = 64 * 16 + PL_PLANE_PAD;  // bytes per plane (64 keys x 16 bytes + padding)
@@ -316,7 +318,6 @@ struct WaveState {
   h8 qf[C::NQB][C::KST];       // Q^T operands (scaled, fp16)
   f4 oacc[C::NQB][2][C::NDT];  // O^T accumulators: [query block][16-query half][16-row d tile]
   float mrun[C::NQB];          // running offset of query l%32 of each block
-  float lsum[C::NQB];          // partial row sums (S layout), when not through the matrix core
   f16v negm[C::NQB];           // -mrun in every accumulator slot: the seed of fast S^T products (no ones column)
   f4 osum[C::NQB][2];          // RSUM: row 0 holds the row sums of the half's 16 queries
   h8 onesA;                    // RSUM: the constant A (row 0 ones: lanes with l % 16 == 0)
@@ -405,7 +406,7 @@ __device__ __forceinline__ void pv_block(const h8 (&va)[C::NDT], const h8 (&pb)[
 // offsets (FIRST: set them from this block).  When an offset moves,
 // `rescale` is set and alpha (S layout) holds the factors the accumulated
 // products of earlier blocks must be multiplied by (the caller applies
-// them); the partial row sums are rescaled here.
+// them, the row sums included).
 template <class C, bool EXACT>
 __device__ __forceinline__ void softmax_block(f16v (&sacc)[C::NQB], WaveState<C>& ws, const LaneCtx& lc, int valid,
                                               bool first, h8 (&pb)[C::NQB][2], float (&alpha)[C::NQB], bool& rescale) {
@@ -444,7 +445,6 @@ __device__ __forceinline__ void softmax_block(f16v (&sacc)[C::NQB], WaveState<C>
         const float mnew = fmaxf(ws.mrun[qb], mx[qb]);
         alpha[qb] = __builtin_amdgcn_exp2f(ws.mrun[qb] - mnew);
         ws.mrun[qb] = mnew;
-        if (!C::RSUM) ws.lsum[qb] *= alpha[qb];
       }
     }
   }
@@ -463,14 +463,6 @@ __device__ __forceinline__ void softmax_block(f16v (&sacc)[C::NQB], WaveState<C>
       for (int x = 0; x < 2; ++x)
         pk[i][x] = pack_h2(__builtin_amdgcn_exp2f(sacc[qb][4 * i + 2 * x]),
                            __builtin_amdgcn_exp2f(sacc[qb][4 * i + 2 * x + 1]));
-    if (!C::ONES && !C::RSUM) {
-      const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-          ws.lsum[qb] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pk[i][x]), one2, ws.lsum[qb], false);
-    }
     u4 b0, b1;  // P^T for queries 0..15 and 16..31 of the block
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
@@ -548,13 +540,12 @@ __device__ __forceinline__ void sched_iteration() {
 // The softmax of one fast block (offset already inside the scores) as a
 // stream of single vector instructions, so that a schedule can place each of
 // them: per query block, 16 exponentials, 8 packs to fp16 (each issued two
-// exponentials after its inputs, so it never waits for them), 4 permlane16
-// swaps that assemble P^T and, without a ones row in V^T, 8 dot products that
-// add the packed probabilities to the row sums.  sm_ops<C>() instructions per
-// query block.
+// exponentials after its inputs, so it never waits for them) and 4
+// permlane16 swaps that assemble P^T.  sm_ops<C>() instructions per query
+// block.
 template <class C>
 constexpr int sm_ops() {
-  return (C::ONES || C::RSUM) ? 28 : 36;
+  return 28;
 }
 template <class C>
 struct FastSoftmax {
@@ -562,7 +553,6 @@ struct FastSoftmax {
   f16v* s;          // [NQB] scores -> exponentials, in place
   unsigned pk[C::NQB][8];
   h8* pb;           // [NQB][2] P^T operands out
-  float* lsum;      // [NQB] row sums (no ones row)
   __device__ __forceinline__ void op(int v) {
     const int qb = v / kSmOps, r = v % kSmOps;
     if (r < 4) {  // exponentials 0..3
@@ -574,9 +564,6 @@ struct FastSoftmax {
     } else if (r < 24) {  // packs 6, 7
       const int i = r - 16;
       pk[qb][i] = pack_h2(s[qb][2 * i], s[qb][2 * i + 1]);
-    } else if (r >= 28) {  // row sums
-      const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
-      lsum[qb] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pk[qb][r - 28]), one2, lsum[qb], false);
     } else {  // swaps: pack (2j+x) with pack (2j+2+x) for j = 0, 2 and x = 0, 1
       const int k = r - 24, x = k & 1, j = (k >> 1) * 4;
       const auto sw = __builtin_amdgcn_permlane16_swap(pk[qb][j + x], pk[qb][j + 2 + x], false, false);
@@ -623,7 +610,6 @@ __device__ __forceinline__ void pipe_iteration_fixed(const char* smem, int vblk,
   FastSoftmax<C> sm;
   sm.s = s_in;
   sm.pb = &p_out[0][0];
-  sm.lsum = ws.lsum;
   int v = 0;
   // Two waves share each SIMD.  The wave in its PV phase (16x16 products, the
   // packs and swaps) runs at raised issue priority, so while one wave streams
@@ -797,7 +783,6 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
       ws.mrun[qb] = 0.f;
-      ws.lsum[qb] = 0.f;
 #pragma unroll
       for (int grp = 0; grp < 2; ++grp)
 #pragma unroll
@@ -924,10 +909,8 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
 #pragma unroll
           for (int grp = 0; grp < 2; ++grp) bad |= !(fabsf(ws.oacc[qb][grp][tl][rl]) <= 3.0e38f);
         }
-      } else if (C::RSUM) {
-        if (lc.g == 0) bad |= !(fabsf(ws.osum[qb][0][0]) <= 3.0e38f) || !(fabsf(ws.osum[qb][1][0]) <= 3.0e38f);
       } else {
-        bad |= !(fabsf(ws.lsum[qb]) <= 3.0e38f);
+        if (lc.g == 0) bad |= !(fabsf(ws.osum[qb][0][0]) <= 3.0e38f) || !(fabsf(ws.osum[qb][1][0]) <= 3.0e38f);
       }
     }
     bad = __any(bad);
@@ -945,18 +928,14 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
   _Float16* ob = p.o + (int64_t)f * p.o_fs + (int64_t)hd * C::D;
 #pragma unroll
   for (int qb = 0; qb < C::NQB; ++qb) {
-    float tot = 0.f;
-    if (!C::ONES && !C::RSUM) tot = ws.lsum[qb] + __shfl_xor(ws.lsum[qb], 32, 64);
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp) {
       float l;
       if (C::ONES) {
         constexpr int tl = C::D / 16, gl = (C::D % 16) / 4, rl = C::D % 4;
         l = __shfl(ws.oacc[qb][grp][tl][rl], 16 * gl + lc.c16, 64);
-      } else if (C::RSUM) {
-        l = __shfl(ws.osum[qb][grp][0], lc.c16, 64);  // row 0: lanes 0..15
       } else {
-        l = __shfl(tot, 16 * grp + lc.c16, 64);
+        l = __shfl(ws.osum[qb][grp][0], lc.c16, 64);  // row 0: lanes 0..15
       }
       const float inv = 1.0f / l;
       const int row = qrow0 + 32 * qb + 16 * grp + lc.c16;
@@ -1093,6 +1072,10 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
   __syncthreads();  // the K/V tile (and the constant plane) and the first Q block are in LDS
 
   WaveState<C> ws;
+  if (C::RSUM) {  // A of the row-sum products: row 0 (lanes with l % 16 == 0) all ones
+    const _Float16 a1 = lc.c16 == 0 ? (_Float16)1.0f : (_Float16)0.0f;
+    ws.onesA = (h8){a1, a1, a1, a1, a1, a1, a1, a1};
+  }
   for (int b = 0; blk < nblk; blk += step, b ^= 1) {
     const bool next = blk + step < nblk;
     if (next) q_issue(blk + step, b ^ 1);  // that buffer's O was read out in the previous block
@@ -1112,16 +1095,15 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
       for (int e = 0; e < 8; ++e) ws.qf[0][st][e] = (_Float16)((float)x[e] * p.c2);
     }
     ws.mrun[0] = 0.f;
-    ws.lsum[0] = 0.f;
 #pragma unroll
-    for (int grp = 0; grp < 2; ++grp)
+    for (int grp = 0; grp < 2; ++grp) {
 #pragma unroll
       for (int t = 0; t < C::NDT; ++t) ws.oacc[0][grp][t] = (f4){0.f, 0.f, 0.f, 0.f};
+      if (C::RSUM) ws.osum[0][grp] = (f4){0.f, 0.f, 0.f, 0.f};
+    }
     tile_step<C, false>(smem, 0, valid, true, ws, lc);
 
     // normalise, round to fp16 (nearest even) into the block buffer
-    float tot = 0.f;
-    if (!C::ONES) tot = ws.lsum[0] + __shfl_xor(ws.lsum[0], 32, 64);
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp) {
       float l;
@@ -1129,7 +1111,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
         constexpr int tl = C::D / 16, gl = (C::D % 16) / 4, rl = C::D % 4;
         l = __shfl(ws.oacc[0][grp][tl][rl], 16 * gl + lc.c16, 64);
       } else {
-        l = __shfl(tot, 16 * grp + lc.c16, 64);
+        l = __shfl(ws.osum[0][grp][0], lc.c16, 64);  // row 0: lanes 0..15
       }
       const float inv = 1.0f / l;
       const int row = 16 * grp + lc.c16;
