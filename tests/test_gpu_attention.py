@@ -296,3 +296,24 @@ def test_short_context_workload_sampled(B, L, C):
     for f, h in [(0, 0), (5, 3), (F - 1, H - 1)]:
         ref = refbank_attention(q, segs, H, frames=[f], head_list=[h], rows=rows)[(f, h)]
         assert_attn_close(got[f][rows][:, h * d:(h + 1) * d], ref, f"expr L={L} f={f} h={h}")
+
+
+def test_prepared_call_matches_direct_call(B):
+    """PreparedAttn (the arguments marshalled once, as the bench's round loop calls
+    the library) gives the same bits as refbank_attn, and the oracle's values."""
+    say("attn prepared call")
+    rng = np.random.default_rng(77)
+    F, L, H, d = 2, 192, 2, 40
+    C = H * d
+    q = rand16(rng, F, L, C)
+    segs = [(rand16(rng, F, L, C), rand16(rng, F, L, C), False), (rand16(rng, 128, C), rand16(rng, 128, C), True)]
+    dq = dev(q)
+    dsegs = [(dev(k), dev(v)) for k, v, _ in segs]
+    direct = B.refbank_attn(dq, dsegs, H)
+    out = torch.empty_like(dq)
+    call = B.PreparedAttn(dq, dsegs, H, out)
+    for _ in range(3):  # repeated launches write the same result
+        call()
+    torch.cuda.synchronize()
+    assert torch.equal(out, direct)
+    assert_attn_close(out.cpu().numpy(), refbank_attention(q, segs, H), "prepared")
