@@ -108,6 +108,32 @@ def test_strided_views_of_fused_qkv(B):
     assert_attn_close(h(out), ref, "strided")
 
 
+@pytest.mark.parametrize("d", [40, 80, 160])
+def test_short_context_strided_views(B, d):
+    """The short-context kernel's row copies on strided views: Q a column slice of
+    a fused [F, L, 3C] projection output, the expression tokens' K/V slices of one
+    [F, 32, 2C] buffer, O written into a wider padded buffer."""
+    say("attn short strided", d)
+    rng = np.random.default_rng(50 + d)
+    F, L, H = 2, 77, 2
+    C = H * d
+    qkv = dev(rand16(rng, F, L, 3 * C))
+    kv = dev(rand16(rng, F, 32, 2 * C))
+    q = qkv[..., :C]
+    k, v = kv[..., :C], kv[..., C:]
+    out = torch.zeros(F, L + 5, C + 16, dtype=torch.float16, device="cuda")
+    view = out[:, :L, 8:8 + C]
+    B.refbank_attn(q, [(k, v)], H, out=view)
+    torch.cuda.synchronize()
+    h = lambda t: t.cpu().numpy()
+    ref = refbank_attention(h(q), [(h(k), h(v), False)], H)
+    assert_attn_close(h(view), ref, f"short strided d{d}")
+    # nothing outside the view was written
+    rest = h(out).copy()
+    rest[:, :L, 8:8 + C] = 0
+    assert not rest.any()
+
+
 def test_segment_order_does_not_matter(B):
     say("attn segment order")
     rng = np.random.default_rng(6)
