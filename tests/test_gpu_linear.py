@@ -118,3 +118,25 @@ def test_projection_then_attention_on_strided_views(B):
     ref = refbank_attention(y16[..., :C], segs, H)
     assert_attn_close(out.cpu().numpy(), ref, "chain")
     assert np.allclose(yb16, ybr, atol=4e-3, rtol=2e-3)
+
+
+@pytest.mark.parametrize("col0", [8, 4], ids=["row stores", "direct stores"])
+@pytest.mark.parametrize("M,N,K", [(700, 192, 320), (16400, 1024, 128)], ids=["128x64 tiles", "256x64 tiles"])
+def test_strided_views(B, M, N, K, col0):
+    """x a column slice of a wider buffer (row pitch K + 64), y written into a
+    padded buffer at column col0 (16-byte aligned rows: LDS-staged stores; 8-byte:
+    direct stores); nothing outside y's view changes."""
+    say("linear strided", M, N, K, col0)
+    x, w, b = case(f"strided{M}", M, N, K, True)
+    xbuf = torch.zeros(M, K + 64, dtype=torch.float16, device="cuda")
+    xbuf[:, 32:32 + K] = dev(x)
+    xv = xbuf[:, 32:32 + K]
+    ybuf = torch.full((M + 2, N + 16), -7.0, dtype=torch.float16, device="cuda")
+    yv = ybuf[1:M + 1, col0:col0 + N]
+    B.linear(xv, dev(w), dev(b), out=yv)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(3).integers(0, M, 200), [0, M - 1]]))
+    check(yv.cpu().numpy()[rows], linear(x[rows], w, b), K)
+    rest = ybuf.cpu().numpy().copy()
+    rest[1:M + 1, col0:col0 + N] = -7.0
+    assert (rest == np.float16(-7.0)).all()
