@@ -319,10 +319,9 @@ __global__ void __launch_bounds__(256, G::MINW) linear_staged_kernel(LinearLaunc
         }
       }
     __syncthreads();
-    // read the thread's chunks in groups of 8, then store them
+    // read the thread's chunks in groups of up to 8, then store them
     constexpr int U = G::BM * CR / 256;
-    static_assert(U % 8 == 0 || U < 8, "store groups");
-    constexpr int UG = U < 8 ? U : 8;
+    constexpr int UG = U % 8 == 0 ? 8 : U % 4 == 0 ? 4 : U % 2 == 0 ? 2 : 1;
 #pragma unroll
     for (int u0 = 0; u0 < U; u0 += UG) {
       h8 v[UG];
@@ -387,14 +386,19 @@ hipError_t launch_linear(const LinearLaunch& a, hipStream_t stream) {
   if (a.K % 64 == 0) {
     // Tile shape by problem shape (measured at the projections of the four
     // UNet levels): 256 x 256 tiles where K is long and they still give about
-    // one workgroup per CU (the contraction-bound case), 256 x 64 where M is
-    // large enough for 1024+ of them, 128 x 64 otherwise.
+    // one workgroup per CU (the contraction-bound case); 128 x 192 where N
+    // allows and M is large enough for 1024+ of them (the fused q/k/v
+    // weights: x is read through L2 a third as often as with 64-wide tiles,
+    // and 5 operand reads feed 6 products); 256 x 64 where M is large enough
+    // for 1024+ of those; 128 x 64 otherwise.
     using Square = GemmCfg<2, 4, 4, 2>;
+    using Wide = GemmCfg<2, 2, 3, 2>;
     using Tall = GemmCfg<4, 2, 2, 2>;
     using Base = GemmCfg<4, 1, 2, 2>;
     auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * (a.N / bn); };
     if (a.K >= 1024 && a.N % Square::BN == 0 && tiles(Square::BM, Square::BN) >= 224)
       return launch_staged<Square>(a, stream);
+    if (a.N % Wide::BN == 0 && tiles(Wide::BM, Wide::BN) >= 1024) return launch_staged<Wide>(a, stream);
     if (tiles(Tall::BM, Tall::BN) >= 1024) return launch_staged<Tall>(a, stream);
     return launch_staged<Base>(a, stream);
   }

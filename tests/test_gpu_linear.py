@@ -56,8 +56,10 @@ def test_linear_full_compare(B, name, M, N, K, bias):
 
 
 # Shapes that select each tile configuration of the K % 64 == 0 kernel
-# (128 x 64, 256 x 64 for large M, 256 x 256 for long K), with ragged row tails.
-TILES = [("128x64 tiles", 333, 128, 128), ("256x64 tiles", 16300, 1024, 128), ("256x256 tiles", 3600, 3840, 1024)]
+# (128 x 64, 256 x 64 for large M, 128 x 192 for large M with N a multiple of
+# 192, 256 x 256 for long K), with ragged row tails.
+TILES = [("128x64 tiles", 333, 128, 128), ("256x64 tiles", 16300, 1024, 128), ("128x192 tiles", 16300, 1920, 640),
+         ("256x256 tiles", 3600, 3840, 1024)]
 
 
 @pytest.mark.parametrize("row_stores", [True, False], ids=["row stores", "direct stores"])
@@ -74,8 +76,8 @@ def test_tile_configs_sampled(B, name, M, N, K, row_stores):
         out = torch.empty((M, N + 4), dtype=torch.float16, device="cuda")[:, :N]
     got = B.linear(dev(x), dev(w), dev(b), out=out)
     torch.cuda.synchronize()
-    # rows around every 256-row tile edge near both ends, plus a random spread
-    edges = [r for t in (256, 512, (M // 256) * 256) for r in (t - 1, t) if r < M]
+    # rows around the 128- and 256-row tile edges near both ends, plus a random spread
+    edges = [r for t in (128, 256, 512, (M // 128) * 128, (M // 256) * 256) for r in (t - 1, t) if r < M]
     rows = np.unique(np.concatenate([np.random.default_rng(M).integers(0, M, 200), [0, M - 1], edges]))
     check(got.cpu().numpy()[rows], linear(x[rows], w, b), K)
 
@@ -121,7 +123,8 @@ def test_projection_then_attention_on_strided_views(B):
 
 
 @pytest.mark.parametrize("col0", [8, 4], ids=["row stores", "direct stores"])
-@pytest.mark.parametrize("M,N,K", [(700, 192, 320), (16400, 1024, 128)], ids=["128x64 tiles", "256x64 tiles"])
+@pytest.mark.parametrize("M,N,K", [(700, 192, 320), (16400, 1024, 128), (26300, 960, 320)],
+                         ids=["128x64 tiles", "256x64 tiles", "128x192 tiles"])
 def test_strided_views(B, M, N, K, col0):
     """x a column slice of a wider buffer (row pitch K + 64), y written into a
     padded buffer at column col0 (16-byte aligned rows: LDS-staged stores; 8-byte:
