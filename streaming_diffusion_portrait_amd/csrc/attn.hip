@@ -8,9 +8,10 @@
 // and never materialises the concatenated keys in HBM.
 //
 // Work decomposition
-//   * one workgroup = 4 wavefronts = one (head, frame, query tile); each wave
-//     owns NQB blocks of 32 query rows (the K/V operands read from LDS serve
-//     all of them, which keeps LDS traffic per score low);
+//   * one workgroup = W wavefronts (4; 8 at d = 80) = one (head, frame,
+//     query tile); each wave owns NQB blocks of 32 query rows (the K/V
+//     operands read from LDS serve all of them, which keeps LDS traffic per
+//     score low);
 //   * K and V tiles of BN = 64 keys are copied HBM -> LDS by direct-to-LDS
 //     loads (global_load_lds_dwordx4) into a ring of NBUF buffers that runs
 //     up to NBUF-1 tiles ahead of the tile being consumed; one barrier per
