@@ -137,13 +137,14 @@ __global__ void __launch_bounds__(64 * kWaves, 2) linear_kernel(LinearLaunch p, 
 // 16-byte chunk c of staged row r sits at slot c ^ ((r / 2) % 8), which puts
 // the 16 rows one read serves on 16 different bank groups.
 //
-// The 4 waves of a workgroup form a WR x (4 / WR) grid; each owns 32 IM rows
+// The W waves of a workgroup form a WR x (W / WR) grid; each owns 32 IM rows
 // x 32 IN features, so per 16-wide step it reads IM + IN operands from LDS for
 // IM x IN products.  Larger wave tiles cut the LDS bytes per product (the LDS,
 // not the matrix core, is what small tiles run out of).
-template <int WR_, int IM_, int IN_, int STAGES_>
+template <int WR_, int IM_, int IN_, int STAGES_, int W_ = 4>
 struct GemmCfg {
-  static constexpr int WR = WR_, WF = 4 / WR_, IM = IM_, IN = IN_, STAGES = STAGES_;
+  static constexpr int W = W_, THREADS = 64 * W_;  // waves per workgroup
+  static constexpr int WR = WR_, WF = W_ / WR_, IM = IM_, IN = IN_, STAGES = STAGES_;
   static constexpr int BM = WR * 32 * IM;          // rows per workgroup
   static constexpr int BN = WF * 32 * IN;          // features per workgroup
   static constexpr int kChunkK = 64;               // K per stage
@@ -151,11 +152,11 @@ struct GemmCfg {
   static constexpr int STAGE_X = BM * kRowB;       // x rows of a stage
   static constexpr int STAGE_B = STAGE_X + BN * kRowB;
   static constexpr int NCOPY = STAGE_B / 1024;     // wave-wide 16-byte copies per stage (8 rows each)
-  static constexpr int CPW = NCOPY / 4;            // per wave
+  static constexpr int CPW = NCOPY / W;            // per wave
   static constexpr int LDS = STAGES * STAGE_B;
   static constexpr int MINW = LDS <= 80 * 1024 ? 2 : 1;  // workgroups per CU the registers are sized for
-  static_assert(WR == 1 || WR == 2 || WR == 4, "2D grid of 4 waves");
-  static_assert(NCOPY % 4 == 0, "copies split evenly over the waves");
+  static_assert(W % WR == 0, "2D grid of waves");
+  static_assert(NCOPY % W == 0, "copies split evenly over the waves");
   static_assert(STAGES >= 2 && CPW * (STAGES - 2) <= 63, "vmcnt range");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
@@ -192,7 +193,7 @@ __device__ __forceinline__ int so(int row, int c) {
 }
 
 template <class G, bool LDS_OUT>
-__global__ void __launch_bounds__(256, G::MINW) linear_staged_kernel(LinearLaunch p, int n_tiles, int total) {
+__global__ void __launch_bounds__(G::THREADS, G::MINW) linear_staged_kernel(LinearLaunch p, int n_tiles, int total) {
   __shared__ __attribute__((aligned(16))) char smem[G::LDS];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -206,7 +207,7 @@ __global__ void __launch_bounds__(256, G::MINW) linear_staged_kernel(LinearLaunc
   const int64_t mw0 = mt * G::BM;  // workgroup's first row
 
   const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)smem;
-  // copy instruction t (this wave issues t = wave, wave + 4, ...) fills staged
+  // copy instruction t (this wave issues t = wave, wave + W, ...) fills staged
   // rows 8t .. 8t+7 (x rows first, then W rows); lane i takes row 8t + i/8 and
   // the chunk whose swizzled slot is i % 8
   auto issue = [&](int stage) {
@@ -214,7 +215,7 @@ __global__ void __launch_bounds__(256, G::MINW) linear_staged_kernel(LinearLaunc
     const unsigned buf = lds0 + (unsigned)((stage % G::STAGES) * G::STAGE_B);
 #pragma unroll
     for (int u = 0; u < G::CPW; ++u) {
-      const int t = wave + 4 * u;
+      const int t = wave + G::W * u;
       const int r = 8 * t + (lane >> 3);
       const int chunk = (lane & 7) ^ ((r >> 1) & 7);
       const _Float16* src;
@@ -320,19 +321,19 @@ __global__ void __launch_bounds__(256, G::MINW) linear_staged_kernel(LinearLaunc
       }
     __syncthreads();
     // read the thread's chunks in groups of up to 8, then store them
-    constexpr int U = G::BM * CR / 256;
+    constexpr int U = G::BM * CR / G::THREADS;
     constexpr int UG = U % 8 == 0 ? 8 : U % 4 == 0 ? 4 : U % 2 == 0 ? 2 : 1;
 #pragma unroll
     for (int u0 = 0; u0 < U; u0 += UG) {
       h8 v[UG];
 #pragma unroll
       for (int u = 0; u < UG; ++u) {
-        const int e = tid + 256 * (u0 + u), row = e / CR, c = e % CR;
+        const int e = tid + G::THREADS * (u0 + u), row = e / CR, c = e % CR;
         v[u] = *reinterpret_cast<const h8*>(smem + row * RB + 16 * so<CR>(row, c));
       }
 #pragma unroll
       for (int u = 0; u < UG; ++u) {
-        const int e = tid + 256 * (u0 + u), row = e / CR, c = e % CR;
+        const int e = tid + G::THREADS * (u0 + u), row = e / CR, c = e % CR;
         const int64_t m = mw0 + row;
         if (m < p.M) *reinterpret_cast<h8*>(p.y + m * p.y_ld + n0 + 8 * c) = v[u];
       }
@@ -372,10 +373,10 @@ hipError_t launch_staged(const LinearLaunch& a, hipStream_t stream) {
   if (total > 0x7fffffff) return hipErrorInvalidValue;
   // 16-byte row stores need y 16-byte aligned with a row pitch of 8 elements
   if ((reinterpret_cast<uintptr_t>(a.y) & 15) == 0 && a.y_ld % 8 == 0)
-    hipLaunchKernelGGL((linear_staged_kernel<G, true>), dim3((unsigned)total), dim3(256), 0, stream, a, n_tiles,
+    hipLaunchKernelGGL((linear_staged_kernel<G, true>), dim3((unsigned)total), dim3(G::THREADS), 0, stream, a, n_tiles,
                        (int)total);
   else
-    hipLaunchKernelGGL((linear_staged_kernel<G, false>), dim3((unsigned)total), dim3(256), 0, stream, a, n_tiles,
+    hipLaunchKernelGGL((linear_staged_kernel<G, false>), dim3((unsigned)total), dim3(G::THREADS), 0, stream, a, n_tiles,
                        (int)total);
   return hipGetLastError();
 }
@@ -386,12 +387,14 @@ hipError_t launch_linear(const LinearLaunch& a, hipStream_t stream) {
   if (a.K % 64 == 0) {
     // Tile shape by problem shape (measured at the projections of the four
     // UNet levels): 256 x 256 tiles where K is long and they still give about
-    // one workgroup per CU (the contraction-bound case); 128 x 192 where N
+    // one workgroup per CU (the contraction-bound case; 8 waves of 64 x 128,
+    // two per SIMD, hide the operand reads that one wave per SIMD could not);
+    // 128 x 192 where N
     // allows and M is large enough for 1024+ of them (the fused q/k/v
     // weights: x is read through L2 a third as often as with 64-wide tiles,
     // and 5 operand reads feed 6 products); 256 x 64 where M is large enough
     // for 1024+ of those; 128 x 64 otherwise.
-    using Square = GemmCfg<2, 4, 4, 2>;
+    using Square = GemmCfg<4, 2, 4, 2, 8>;
     using Wide = GemmCfg<2, 2, 3, 2>;
     using Tall = GemmCfg<4, 2, 2, 2>;
     using Base = GemmCfg<4, 1, 2, 2>;
