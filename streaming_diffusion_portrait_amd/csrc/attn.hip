@@ -812,7 +812,15 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
       if (C::ONES) {
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) ok &= fabsf(ws.mrun[qb]) <= kFastMaxOffset;
-        ok = __all(ok);
+        // One decision for the whole workgroup: the waves share the copies of
+        // every tile and its barriers, so they must all take the same path.
+        const bool wave_ok = __all(ok);
+        if (lc.lane == 0) flags[wave] = wave_ok ? 1 : 0;
+        __syncthreads();
+        int all_ok = 1;
+#pragma unroll
+        for (int w = 0; w < C::W; ++w) all_ok &= flags[w];
+        ok = __builtin_amdgcn_readfirstlane(all_ok) != 0;
         if (ok && lc.h) {
 #pragma unroll
           for (int qb = 0; qb < C::NQB; ++qb) ws.qf[qb][C::KST - 1][0] = (_Float16)(-ws.mrun[qb]);  // offset joins the product

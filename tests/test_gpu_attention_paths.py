@@ -140,3 +140,34 @@ def test_huge_scores_exact_tiles(B, name, d, F, L, H, lk, qg, kg, kstar):
     ref = refbank_attention(q, segs, H)
     assert np.allclose(ref[0], np.asarray(v[0][jstar], np.float64)[None, :], atol=1e-6)
     assert_attn_close(got, ref, name)
+
+
+# One workgroup (256 query rows at d = 40) whose waves disagree about
+# freezing: one wave's 64 rows have offsets far beyond +-1024 (they stay
+# exact), the other waves' rows are ordinary.  The key sequence (8 whole
+# tiles) is longer than the copy ring, so tiles are copied inside the loop;
+# the workgroup must take one path for all of its waves.
+MIXED = [("huge rows in the first wave", 0), ("huge rows in the last wave", 192)]
+
+
+@pytest.mark.parametrize("name,row0", MIXED, ids=[c[0] for c in MIXED])
+def test_mixed_offsets_in_one_workgroup(B, name, row0):
+    say("attn path mixed offsets", name)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    F, L, H, d, lk = 1, 256, 1, 40, 512
+    q = rng.standard_normal((F, L, d), dtype=np.float32)
+    q[:, row0:row0 + 64, :] = 40.0
+    k = 20.0 + rng.standard_normal((F, lk, d), dtype=np.float32)
+    jstar = int(rng.integers(64, lk))
+    k[:, jstar, :] = 40.0
+    q, k = q.astype(np.float16), k.astype(np.float16)
+    v = rng.standard_normal((F, lk, d), dtype=np.float32).astype(np.float16)
+    segs = [(k, v, False)]
+    scale = d ** -0.5 * np.log2(np.e)
+    s = np.asarray(q[0], np.float64) @ np.asarray(k[0], np.float64).T * scale
+    m0 = s[:, :64].max(axis=1)
+    assert np.abs(m0[row0:row0 + 64]).min() > 1024.0
+    others = np.r_[0:row0, row0 + 64:L]
+    assert np.abs(m0[others]).max() < 1024.0
+    got = run_gpu(B, q, segs, H)
+    assert_attn_close(got, refbank_attention(q, segs, H), name)
