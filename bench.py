@@ -394,16 +394,22 @@ def main():
 
 
 def cpu_baseline(lay0, F, H, m):
-    """Time the fp64 oracle on a sample of the first 64^2 layer and compare it with the GPU output."""
+    """Time the fp64 oracle on a sample of the first 64^2 layer and compare it with the GPU output.
+
+    A thread pool runs (frame, head) pairs side by side with one BLAS thread per
+    worker; workers = the host cores this process may use, capped by
+    OMP_NUM_THREADS (the CPU share a GPU job is given).  One pair is timed first
+    to size the sample (about 4 s per pass), then the same pairs run three
+    times; the median pass is reported.
+    """
+    import concurrent.futures
+
     import numpy as np
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    affinity = len(os.sched_getaffinity(0))
+    workers = max(1, min(affinity, int(os.environ.get("OMP_NUM_THREADS", affinity))))
     host = lay0["host"]
     segs = [(host["k_self"], host["v_self"], False)]
     segs += [(k, v, True) for k, v in zip(host["bank_k"], host["bank_v"])]
@@ -411,25 +417,51 @@ def cpu_baseline(lay0, F, H, m):
     L, C = lay0["L"], lay0["C"]
     d = C // H
     lk = lay0["lk"]
-    pairs_done, flops, err_max = 0, 0, 0.0
-    budget_s, t0 = 12.0, time.perf_counter()
-    rng = np.random.default_rng(0)
-    order = rng.permutation(F * H)
-    for idx in order:
+    chunk = 1024  # query rows per oracle call: bounds each worker's score matrix to 1024 x keys fp64
+
+    def one_pair(idx):
         f, h = divmod(int(idx), H)
-        ref = oracle.refbank_attention(host["q"], segs, H, frames=[f], head_list=[h])[(f, h)]
-        pairs_done += 1
-        flops += 4 * L * lk * d
-        err_max = max(err_max, float(np.abs(got[f][:, h * d:(h + 1) * d].astype(np.float64) - ref).max()))
-        if time.perf_counter() - t0 > budget_s:
-            break
-    sec = time.perf_counter() - t0
-    log(f"  cpu oracle: {pairs_done} (frame, head) pairs in {sec:.1f}s on {threads} threads, "
+        err = 0.0
+        for r0 in range(0, L, chunk):
+            rows = np.arange(r0, min(L, r0 + chunk))
+            ref = oracle.refbank_attention(host["q"], segs, H, frames=[f], head_list=[h], rows=rows)[(f, h)]
+            err = max(err, float(np.abs(got[f][rows, h * d:(h + 1) * d].astype(np.float64) - ref).max()))
+        return err
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover - threadpoolctl ships with the image
+        threadpool_limits = None
+    order = np.random.default_rng(0).permutation(F * H)
+    passes, err_max = [], 0.0
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx is not None:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        err_max = one_pair(order[0])
+        t_pair = time.perf_counter() - t0
+        n_pairs = int(min(F * H, max(workers, round(workers * 4.0 / max(t_pair, 1e-3)))))
+        sample = order[:n_pairs]
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            for _ in range(3):
+                t0 = time.perf_counter()
+                errs = list(ex.map(one_pair, sample))
+                passes.append(time.perf_counter() - t0)
+                err_max = max([err_max] + errs)
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    sec = float(np.median(passes))
+    flops = 4 * L * lk * d * n_pairs
+    log(f"  cpu oracle: {n_pairs} (frame, head) pairs per pass on {workers} workers (1 BLAS thread each, "
+        f"{affinity} cores in the affinity mask), passes {', '.join(f'{p:.1f}' for p in passes)} s, "
         f"max|gpu - oracle| {err_max:.2e}")
-    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"{pairs_done} of {F * H} (frame, head) pairs of the first 64^2 layer "
-                       f"(L=4096, d={d}, keys={lk}), fp64 NumPy, {sec:.1f} s"),
-            "seconds": round(sec, 2), "max_abs_err_gpu_vs_oracle": err_max}
+    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": int(workers), "kind": "oracle",
+            "sample": (f"{n_pairs} of {F * H} (frame, head) pairs of the first 64^2 layer (L={L}, d={d}, "
+                       f"keys={lk}), fp64 NumPy oracle in a {workers}-thread pool with one BLAS thread each, "
+                       f"median of 3 passes ({', '.join(f'{p:.1f}' for p in passes)} s)"),
+            "seconds": round(sec, 2), "affinity_cores": affinity, "max_abs_err_gpu_vs_oracle": err_max}
 
 
 if __name__ == "__main__":

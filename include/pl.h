@@ -91,7 +91,11 @@ size_t pl_refbank_attn_workspace_size(int32_t F, int32_t Lq, int32_t H, int32_t 
                                       const int64_t* seg_len, int32_t nseg);
 
 /* Launch one reference-bank attention layer.
- *   q, o          device fp16 [F][Lq][ld]; o must not overlap q or any K/V.
+ *   q, o          device fp16 [F][Lq][ld]; o must not overlap q or any K/V
+ *                 (checked: PL_EINVAL when o's address range meets that of q or
+ *                 of a segment's k or v, unless the two share a row stride, the
+ *                 frame strides are whole rows, and their column ranges within
+ *                 a row are disjoint -- column slices of one fused buffer).
  *   q_ld, o_ld    row strides in elements (>= H*d, multiple of 8).
  *   *_frame_stride  elements between frames (>= Lq*ld is not required, but
  *                 rows of different frames must not overlap in o).
@@ -240,9 +244,11 @@ pl_status pl_lerp_points(const float* a, const float* b, int64_t D, int32_t n, f
  * most three times per stream.  Section 三条条件通路: the embedding is the
  * 512-dimensional MotEncoder output.
  *
- * For each query i: min_dist[i] = min_j ||query[i] - bank[j]||_2 (Euclidean,
- * fp32, fixed reduction order), argmin[i] = the lowest j reaching it,
- * exceeds[i] = (min_dist[i] > threshold) ? 1 : 0.
+ * For each query i, with the Euclidean distances d_j = ||query[i] - bank[j]||_2
+ * accumulated in fp64 (each fp32 difference and its square are exact there;
+ * the sum has a fixed reduction order): argmin[i] = the lowest j reaching
+ * min_j d_j, exceeds[i] = (min_j d_j > threshold) ? 1 : 0 decided in fp64,
+ * min_dist[i] = min_j d_j rounded to fp32.
  *
  *   query         device fp32 [nq][D]; bank device fp32 [n][D].
  *   nq >= 1; n in 1..PL_MAX_MOTION_BANK; D in 1..65536.

@@ -215,24 +215,34 @@ def _rows(t, name):
     raise ValueError(f"{name} must be [F, L, C] or [L, C]")
 
 
-def make_segments(segments):
+def make_segments(segments, frames=None, channels=None):
     """Segment table for the key axis (the bank segment assembly).
 
     ``segments``: sequence of ``(k, v)`` fp16 device tensors, either
-    ``[F, Ls, C]`` (per-frame: the frame's own tokens) or ``[Ls, C]`` (shared
-    by every frame: the reference entry and anchors).  Nothing is copied; the
-    table holds pointers and strides.  Returns ``(array, keepalive)``.
+    ``[F, Ls, C]`` (per-frame: the frame's own tokens), ``[1, Ls, C]`` or
+    ``[Ls, C]`` (shared by every frame: the reference entry and anchors).
+    ``frames`` / ``channels``: the query's F and C; a 3-D segment must have
+    F or 1 frames and every segment C columns (checked here, since the
+    library never sees a segment's extent).  Nothing is copied; the table
+    holds pointers and strides.  Returns ``(array, keepalive)``.
     """
     n = len(segments)
     if not 1 <= n <= PL_MAX_SEGMENTS:
         raise ValueError(f"1..{PL_MAX_SEGMENTS} segments required")
     arr = (pl_kv_segment * n)()
     for i, (k, v) in enumerate(segments):
-        _need(k, torch.float16, "k")
-        _need(v, torch.float16, "v")
         if k.shape != v.shape or k.stride() != v.stride():
             raise ValueError("k and v of a segment must share shape and strides")
+        if channels is not None and k.shape[-1] != channels:
+            raise ValueError(f"segment {i} has {k.shape[-1]} columns, q has {channels}")
         ld, fs = _rows(k, "k")
+        if k.dim() == 3:
+            if k.shape[0] == 1 and frames != 1:
+                fs = 0  # one set of rows for every frame
+            elif frames is not None and k.shape[0] != frames:
+                raise ValueError(f"segment {i} has {k.shape[0]} frames, q has {frames} (or pass 1 to share)")
+        _need(k, torch.float16, "k")
+        _need(v, torch.float16, "v")
         arr[i] = pl_kv_segment(k.data_ptr(), v.data_ptr(), k.shape[-2], ld, fs)
     return arr, segments
 
@@ -259,7 +269,7 @@ def refbank_attn(q, segments, heads, out=None, scale=None, stream=None):
         scale = d ** -0.5
     q_ld, q_fs = _rows(q, "q")
     o_ld, o_fs = _rows(out, "out")
-    segs, _keep = make_segments(segments)
+    segs, _keep = make_segments(segments, F, C)
     lens = (ctypes.c_int64 * len(segments))(*[s.len for s in segs])
     ws = load().pl_refbank_attn_workspace_size(F, L, heads, d, lens, len(segments))
     if ws:
@@ -352,6 +362,17 @@ def pile_prefill(ref, n_windows, seed, step_len=333, alphas_cumprod=None, out=No
     return out
 
 
+def _as_rows(t, n, name):
+    """``t`` [..., n] seen as a [rows, n] matrix with one row stride, without a copy."""
+    if t.dim() == 2:
+        return t
+    try:
+        return t.view(-1, n)
+    except RuntimeError as e:
+        raise ValueError(f"{name} cannot be seen as [rows, {n}] with one row stride "
+                         f"(strides {t.stride()}); pass a 2-D view") from e
+
+
 def linear(x, w, bias=None, out=None, stream=None):
     """y = x W^T (+ bias) (see ``pl_linear``).
 
@@ -359,25 +380,32 @@ def linear(x, w, bias=None, out=None, stream=None):
     axes; rows may be strided); ``w``: fp16 ``[N, K]``; ``bias``: fp32 ``[N]``
     or None.  Returns ``out`` ``[..., N]`` (allocated if None).
     """
-    _need(x, torch.float16, "x")
-    _need(w, torch.float16, "w")
     if x.stride(-1) != 1 or w.dim() != 2 or w.stride(-1) != 1:
         raise ValueError("x and w need unit stride in their last dimension; w must be [N, K]")
-    lead = x.shape[:-1]
+    lead = tuple(x.shape[:-1])
     K = x.shape[-1]
-    x2 = x.reshape(-1, K) if x.dim() != 2 else x
-    M = x2.shape[0]
     N = w.shape[0]
     if w.shape[1] != K:
         raise ValueError("w must be [N, K] with x's K")
+    # views, never copies: rows that cannot be seen as one [M, K] / [M, N] matrix raise
+    x2 = _as_rows(x, K, "x")
+    M = x2.shape[0]
+    if out is not None:
+        if tuple(out.shape) != (*lead, N):
+            raise ValueError(f"out must have shape {(*lead, N)}, got {tuple(out.shape)}")
+        if out.stride(-1) != 1:
+            raise ValueError("out needs unit stride in its last dimension")
+        y2 = _as_rows(out, N, "out")
+    if bias is not None and (not bias.is_contiguous() or bias.numel() != N):
+        raise ValueError("bias must be contiguous [N]")
+    _need(x, torch.float16, "x")
+    _need(w, torch.float16, "w")
     if out is None:
         out = torch.empty((*lead, N), dtype=torch.float16, device=x.device)
+        y2 = _as_rows(out, N, "out")
     _need(out, torch.float16, "out")
-    y2 = out.reshape(-1, N) if out.dim() != 2 else out
     if bias is not None:
         _need(bias, torch.float32, "bias")
-        if not bias.is_contiguous() or bias.numel() != N:
-            raise ValueError("bias must be contiguous [N]")
     _check("pl_linear", pl_linear(ctypes.c_void_p(x2.data_ptr()), x2.stride(0), ctypes.c_void_p(w.data_ptr()),
                                   w.stride(0), ctypes.c_void_p(bias.data_ptr()) if bias is not None else None,
                                   ctypes.c_void_p(y2.data_ptr()), y2.stride(0), M, N, K, _stream_ptr(stream)))
@@ -477,7 +505,7 @@ class PreparedAttn:
             scale = d ** -0.5
         q_ld, q_fs = _rows(q, "q")
         o_ld, o_fs = _rows(out, "out")
-        self._segs, self._keep = make_segments(segments)
+        self._segs, self._keep = make_segments(segments, F, C)
         self._tensors = (q, out)
         lens = (ctypes.c_int64 * len(segments))(*[s.len for s in self._segs])
         if load().pl_refbank_attn_workspace_size(F, L, heads, d, lens, len(segments)):

@@ -23,6 +23,8 @@ HIPCC_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-Wall",
+    "-Wextra",
+    "-Werror",
     # no packed-fp32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

@@ -732,7 +732,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
   // for every key -- K's column D is ones (it meets the offset column of Q),
   // V^T's row D is ones (its products are the row sums).  The copies never
   // write this plane; the first barrier below publishes it.
-  if (C::ONES) {
+  if constexpr (C::ONES) {
     for (int i = tid >> 6; i < 2 * C::NBUF; i += C::W) {
       h8 one = {0, 0, 0, 0, 0, 0, 0, 0};
       one[0] = (_Float16)1.0f;
@@ -742,7 +742,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
   // K step st: lane half h reads plane 2st+h at key c32.  V^T read r of lane
   // (g, c16): key vrow(g) + 16r + c16/4, dims 4(c16%4)..+3 of the 16-dim tile,
   // i.e. plane 2t + (c16%4)/2, byte 8*(c16%2) of the key's chunk.
-  if (C::RSUM) {  // A of the row-sum products: row 0 (lanes with l % 16 == 0) all ones
+  if constexpr (C::RSUM) {  // A of the row-sum products: row 0 (lanes with l % 16 == 0) all ones
     const _Float16 a1 = lc.c16 == 0 ? (_Float16)1.0f : (_Float16)0.0f;
     ws.onesA = (h8){a1, a1, a1, a1, a1, a1, a1, a1};
   }
@@ -788,8 +788,8 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
       for (int grp = 0; grp < 2; ++grp)
 #pragma unroll
         for (int t = 0; t < C::NDT; ++t) ws.oacc[qb][grp][t] = (f4){0.f, 0.f, 0.f, 0.f};
-      if (C::RSUM) ws.osum[qb][0] = ws.osum[qb][1] = (f4){0.f, 0.f, 0.f, 0.f};
-      if (C::ONES && lc.h) ws.qf[qb][C::KST - 1][0] = (_Float16)0.0f;  // offset column: none yet
+      if constexpr (C::RSUM) ws.osum[qb][0] = ws.osum[qb][1] = (f4){0.f, 0.f, 0.f, 0.f};
+      if constexpr (C::ONES) if (lc.h) ws.qf[qb][C::KST - 1][0] = (_Float16)0.0f;  // offset column: none yet
     }
 
     cp.s = 0;
@@ -809,7 +809,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
     bool fast = false;
     if (!exact_all) {
       bool ok = true;
-      if (C::ONES) {
+      if constexpr (C::ONES) {
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) ok &= fabsf(ws.mrun[qb]) <= kFastMaxOffset;
         // One decision for the whole workgroup: the waves share the copies of
@@ -912,7 +912,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
-      if (C::ONES) {
+      if constexpr (C::ONES) {
         constexpr int tl = C::D / 16, gl = (C::D % 16) / 4, rl = C::D % 4;
         if (lc.g == gl) {
 #pragma unroll
@@ -940,7 +940,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp) {
       float l;
-      if (C::ONES) {
+      if constexpr (C::ONES) {
         constexpr int tl = C::D / 16, gl = (C::D % 16) / 4, rl = C::D % 4;
         l = __shfl(ws.oacc[qb][grp][tl][rl], 16 * gl + lc.c16, 64);
       } else {
@@ -1034,7 +1034,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
   const int f = fs / nsplit;
   const int split = fs - f * nsplit;
 
-  if (C::ONES) {  // the constant plane of the one K tile and the one V tile
+  if constexpr (C::ONES) {  // the constant plane of the one K tile and the one V tile
     for (int i = tid >> 6; i < 2; i += C::W) {
       h8 one = {0, 0, 0, 0, 0, 0, 0, 0};
       one[0] = (_Float16)1.0f;
@@ -1081,7 +1081,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
   __syncthreads();  // the K/V tile (and the constant plane) and the first Q block are in LDS
 
   WaveState<C> ws;
-  if (C::RSUM) {  // A of the row-sum products: row 0 (lanes with l % 16 == 0) all ones
+  if constexpr (C::RSUM) {  // A of the row-sum products: row 0 (lanes with l % 16 == 0) all ones
     const _Float16 a1 = lc.c16 == 0 ? (_Float16)1.0f : (_Float16)0.0f;
     ws.onesA = (h8){a1, a1, a1, a1, a1, a1, a1, a1};
   }
@@ -1108,7 +1108,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
     for (int grp = 0; grp < 2; ++grp) {
 #pragma unroll
       for (int t = 0; t < C::NDT; ++t) ws.oacc[0][grp][t] = (f4){0.f, 0.f, 0.f, 0.f};
-      if (C::RSUM) ws.osum[0][grp] = (f4){0.f, 0.f, 0.f, 0.f};
+      if constexpr (C::RSUM) ws.osum[0][grp] = (f4){0.f, 0.f, 0.f, 0.f};
     }
     tile_step<C, false>(smem, 0, valid, true, ws, lc);
 
@@ -1116,7 +1116,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp) {
       float l;
-      if (C::ONES) {
+      if constexpr (C::ONES) {
         constexpr int tl = C::D / 16, gl = (C::D % 16) / 4, rl = C::D % 4;
         l = __shfl(ws.oacc[0][grp][tl][rl], 16 * gl + lc.c16, 64);
       } else {

@@ -4,11 +4,15 @@
 // embedding is compared with every motion-bank entry; the smallest Euclidean
 // distance decides whether an anchor is appended (distance above 17).
 //
-// One wavefront per query.  Lane l accumulates the squared differences of
-// elements l, l+64, l+128, ... in fp32 for every bank entry, then the wave
-// reduces the 64 partial sums with a fixed xor-butterfly, so the result is
-// the same on every run.  Lane 0 takes sqrt, the minimum (lowest index on
-// ties) and the strict comparison with the threshold.
+// One wavefront per query.  The inputs are fp32; each difference and its
+// square are exact in fp64, and lane l sums the squares of elements l, l+64,
+// l+128, ... in fp64 for every bank entry; the wave then reduces the 64
+// partial sums with a fixed xor-butterfly, so the result is the same on every
+// run and within a few fp64 ulps of the exact distance.  The minimum (lowest
+// index on ties) and the strict comparison with the threshold are taken on
+// the fp64 distances, so the decision only differs from an exact evaluation
+// when a distance lies within about 1e-15 relative of the threshold; the
+// reported minimum is that distance rounded to fp32.
 #include "pl_internal.h"
 
 namespace pl {
@@ -16,7 +20,7 @@ namespace {
 
 constexpr int kWave = 64;
 
-__device__ inline float wave_sum(float v) {
+__device__ inline double wave_sum(double v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
   return v;
@@ -29,9 +33,9 @@ motion_min_l2_kernel(const float* __restrict__ query, const float* __restrict__ 
   const int qi = blockIdx.x;
   const int lane = threadIdx.x;
   const float* q = query + (int64_t)qi * D;
-  float part[PL_MAX_MOTION_BANK];
+  double part[PL_MAX_MOTION_BANK];
 #pragma unroll
-  for (int j = 0; j < PL_MAX_MOTION_BANK; ++j) part[j] = 0.f;
+  for (int j = 0; j < PL_MAX_MOTION_BANK; ++j) part[j] = 0.0;
   // Every entry slot is read without a branch (slots past n re-read the last
   // entry; their sums are ignored) and the loop is unrolled, so the loads of 8
   // strides (all of a 512-d embedding) are in flight together instead of one
@@ -41,19 +45,19 @@ motion_min_l2_kernel(const float* __restrict__ query, const float* __restrict__ 
   for (int j = 0; j < PL_MAX_MOTION_BANK; ++j) brow[j] = bank + (int64_t)min(j, n - 1) * D;
 #pragma unroll 8
   for (int k = lane; k < D; k += kWave) {
-    const float qv = q[k];
+    const double qv = q[k];
 #pragma unroll
     for (int j = 0; j < PL_MAX_MOTION_BANK; ++j) {
-      const float diff = qv - brow[j][k];
-      part[j] = fmaf(diff, diff, part[j]);
+      const double diff = qv - (double)brow[j][k];
+      part[j] = fma(diff, diff, part[j]);
     }
   }
-  float best = 0.f;
+  double best = 0.0;
   int best_j = 0;
 #pragma unroll
   for (int j = 0; j < PL_MAX_MOTION_BANK; ++j) {
     if (j < n) {
-      const float dist = sqrtf(wave_sum(part[j]));
+      const double dist = sqrt(wave_sum(part[j]));
       if (j == 0 || dist < best) {
         best = dist;
         best_j = j;
@@ -61,9 +65,9 @@ motion_min_l2_kernel(const float* __restrict__ query, const float* __restrict__ 
     }
   }
   if (lane == 0) {
-    min_dist[qi] = best;
+    min_dist[qi] = (float)best;
     argmin[qi] = best_j;
-    exceeds[qi] = best > threshold ? 1 : 0;
+    exceeds[qi] = best > (double)threshold ? 1 : 0;
   }
 }
 

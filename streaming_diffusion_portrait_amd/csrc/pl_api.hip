@@ -32,6 +32,34 @@ pl_status device_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A strided fp16 view: rows of `width` elements, `ld` apart, in `frames`
+// frames `fs` apart (fs = 0: one set of rows shared by every frame).
+struct View {
+  const void* p;
+  int64_t ld, fs, rows, frames, width;
+};
+
+// May two views share an element?  Their byte ranges are compared first;
+// when those meet, two views with the same row stride whose frame strides are
+// whole rows are still disjoint if their column ranges within a row (taken
+// modulo the row stride) do not meet -- the case of column slices of one
+// fused buffer.  Anything else that meets is reported as overlapping.
+bool views_may_overlap(const View& a, const View& b) {
+  auto span = [](const View& v) {
+    const int64_t nf = v.fs == 0 ? 1 : v.frames;
+    return ((nf - 1) * v.fs + (v.rows - 1) * v.ld + v.width) * (int64_t)sizeof(uint16_t);
+  };
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  const uintptr_t a1 = a0 + (uintptr_t)span(a), b1 = b0 + (uintptr_t)span(b);
+  if (a1 <= b0 || b1 <= a0) return false;
+  if (a.ld == b.ld && a.fs % a.ld == 0 && b.fs % b.ld == 0) {
+    const int64_t diff = (int64_t)(a0 - b0);  // bytes; both views are 16-byte aligned
+    const int64_t c = ((diff / 2) % a.ld + a.ld) % a.ld;  // a's first column relative to b's, modulo a row
+    if (c >= b.width && c + a.width <= a.ld) return false;
+  }
+  return true;
+}
+
 // Stable Diffusion's scaled_linear schedule: beta_i = (s0 + i*(s1-s0)/(T-1))^2
 // with s0 = sqrt(0.00085), s1 = sqrt(0.012), alpha_bar_t = prod_{i<=t}(1 - beta_i).
 struct SdSchedule {
@@ -187,6 +215,16 @@ pl_status pl_refbank_attn(const void* q, int64_t q_ld, int64_t q_frame_stride, v
     a.seg[i].len = s.len;
     a.seg[i].ld = s.ld;
     a.seg[i].frame_stride = s.frame_stride;
+  }
+  // o is written while q and every K/V row are still being read
+  const View vo{o, o_ld, o_frame_stride, Lq, F, width};
+  if (views_may_overlap(vo, View{q, q_ld, q_frame_stride, Lq, F, width}))
+    return fail(PL_EINVAL, "pl_refbank_attn: o overlaps q");
+  for (int i = 0; i < nseg; ++i) {
+    const pl_kv_segment& s = segs[i];
+    if (views_may_overlap(vo, View{s.k, s.ld, s.frame_stride, s.len, F, width}) ||
+        views_may_overlap(vo, View{s.v, s.ld, s.frame_stride, s.len, F, width}))
+      return fail(PL_EINVAL, "pl_refbank_attn: o overlaps the keys or values of segment %d", i);
   }
   if (total > (int64_t(1) << 24)) return fail(PL_EINVAL, "pl_refbank_attn: total key length exceeds 2^24");
   a.q = static_cast<const _Float16*>(q);

@@ -101,6 +101,33 @@ def test_attention_second_segment_checked(lib):
     assert "segment 1" in B.last_error()
 
 
+def test_attention_rejects_output_overlap(lib):
+    # o is the q buffer itself, or o sits on a segment's values
+    big = _segs((ctypes.c_void_p(0x900000), ctypes.c_void_p(0xA00000), 256, 64, 0))
+    assert _attn(o=A, segs=big) == B.PL_EINVAL and "o overlaps q" in B.last_error()
+    assert _attn(o=ctypes.c_void_p(0xA00000 + 64 * 2 * 8), segs=big) == B.PL_EINVAL
+    assert "segment 0" in B.last_error()
+    assert _attn(o=ctypes.c_void_p(0xA00000), segs=big) == B.PL_EINVAL
+    assert "segment 0" in B.last_error()
+
+
+def test_attention_fused_column_slices(lib):
+    # q | k | v | o as column slices of one [F, L, 4C] buffer (row stride 4C):
+    # the views interleave in memory but share no element, so the overlap
+    # check passes and the call stops at the next check (total key length)
+    F, L, C = 2, 16, 64
+    base = 0x400000
+    ld, fs = 4 * C, 4 * C * L
+    q, k, v, o = (ctypes.c_void_p(base + 2 * C * i) for i in range(4))
+    too_long = _segs((k, v, (1 << 24) + 1, ld, fs))
+    st = B.pl_refbank_attn(q, ld, fs, o, ld, fs, F, L, 2, 32, too_long, 1, 0.17, None, 0, None)
+    assert st == B.PL_EINVAL and "total key length" in B.last_error()
+    # the same buffer with o shifted half a slice into v's columns overlaps
+    o_bad = ctypes.c_void_p(base + 2 * C * 2 + C)
+    st = B.pl_refbank_attn(q, ld, fs, o_bad, ld, fs, F, L, 2, 32, too_long, 1, 0.17, None, 0, None)
+    assert st == B.PL_EINVAL and "segment 0" in B.last_error()
+
+
 def test_workspace_size_is_zero(lib):
     lens = (ctypes.c_int64 * 2)(4096, 4096)
     assert lib.pl_refbank_attn_workspace_size(16, 4096, 8, 40, lens, 2) == 0

@@ -116,7 +116,7 @@ def test_ddim_recovers_x0_from_forward_marginal(B):
     assert np.max(np.abs(host(x0_out).reshape(4, 4, 64, 64) - x0[12:16])) <= 1e-5
 
 
-def _motion_check(B, bank, queries, threshold=17.0, margin=1e-3):
+def _motion_check(B, bank, queries, threshold=17.0, margin=1e-9):
     md, am, ex = B.motion_bank_min_l2(dev(queries), dev(bank), threshold)
     md, am, ex = host(md), host(am), host(ex)
     rd, ra, rf = motion_bank_min_l2(queries, bank, threshold)
