@@ -124,6 +124,120 @@ def one_layer(args, B, todev, m, F, H):
                       "pct_fp16_peak": round(100 * tf / PEAK_FP16_TFLOPS, 2)}), flush=True)
 
 
+def build_round(B, inputs, todev, m, F, H, dev, keep_host=True):
+    """One round's device state at anchor count m: fresh seeded tensors for the
+    16 attention layers (prepared calls), the 16x4x64x64 pile, the motion bank."""
+    import torch
+
+    layers = []
+    for li, (name, L, C) in enumerate(inputs.SD15_LAYERS):
+        lay = inputs.attention_layer(1000 * SEED + li, F, L, C, m)
+        q = todev(lay["q"])
+        segs = [(todev(lay["k_self"]), todev(lay["v_self"]))]
+        segs += [(todev(k), todev(v)) for k, v in zip(lay["bank_k"], lay["bank_v"])]
+        out = torch.empty_like(q)
+        lk = L * (2 + m)
+        layers.append(dict(name=name, L=L, C=C, d=C // H, lk=lk, q=q, segs=segs, out=out,
+                           call=B.PreparedAttn(q, segs, H, out), host=lay if (li == 0 and keep_host) else None,
+                           flops=attention_flops(F, L, C, lk), bytes=attention_bytes(F, L, C, m)))
+    x_t_np, eps_np = inputs.ddim_pile(SEED, (16, 4, 64, 64))
+    R = dict(layers=layers, m=m, x_t=todev(x_t_np), eps=todev(eps_np))
+    R["x_prev"] = torch.empty_like(R["x_t"])
+    R["x0"] = torch.empty((4, 4, 64, 64), dtype=torch.float32, device=dev)
+    bank_np, q_np, _ = inputs.motion_bank(SEED, 1 + m, 512, nq=1)
+    R["mb"], R["mq"] = todev(bank_np), todev(q_np)
+    R["md"] = (torch.empty(1, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
+               torch.empty(1, dtype=torch.uint8, device=dev))
+    R["pile"] = B.Pile(4, 333)
+    R["next_window"] = 4  # ids 0..2 prefilled, 3 enters with the first round
+    return R
+
+
+def eager_round(B, R, events=None):
+    """The round as separate library calls from the host: the 16 attention layers,
+    the rolling DDIM step (which also draws the next window's noise into the
+    leaving window's slot) with the host pile state machine, the drift check."""
+    for li, lay in enumerate(R["layers"]):
+        if events is not None:
+            events[li][0].record()
+        lay["call"]()
+        if events is not None:
+            events[li][1].record()
+    _, t_slot, emit = R["pile"].begin_round()
+    B.pyramid_ddim_step(R["x_t"], R["eps"], t_slot, x_prev=R["x_prev"], x0_out=R["x0"], emit_window=emit,
+                        roll=(SEED, R["next_window"]))
+    R["next_window"] += 1
+    R["pile"].end_round()
+    B.motion_bank_min_l2(R["mq"], R["mb"], 17.0, out=R["md"])
+
+
+def time_eager_rounds(R, warmup, K):
+    """K eager rounds bracketed by synchronisations, HIP events around every
+    attention launch.  Returns (ms per round, per-layer ms)."""
+    import numpy as np
+    import torch
+
+    from streaming_diffusion_portrait_amd import binding as B
+    for _ in range(warmup):
+        eager_round(B, R)
+    torch.cuda.synchronize()
+    nl = len(R["layers"])
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(nl)]
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(K):
+        eager_round(B, R, evs[k])
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t_start) / K
+    per_layer = [float(np.mean([evs[k][li][0].elapsed_time(evs[k][li][1]) for k in range(K)])) for li in range(nl)]
+    return ms, per_layer
+
+
+def time_graph_rounds(B, R, warmup, K):
+    """The round with its pile state on the device, captured once as a graph and
+    replayed K times (one host call per round).  Also returns the host time to
+    issue one round: the graph replay against the eager sequence of calls."""
+    import torch
+
+    dpile = B.DevicePile(4, 333)
+    xg = R["x_t"].clone()  # the graph's own pile, rolled in place
+    x0g = torch.empty_like(R["x0"])
+
+    def dev_round(stream):
+        for lay in R["layers"]:
+            lay["call"](stream)
+        dpile.step(xg, R["eps"], xg, x0g, SEED, stream=stream)
+        B.motion_bank_min_l2(R["mq"], R["mb"], 17.0, out=R["md"], stream=stream)
+
+    dev_round(torch.cuda.current_stream())  # every kernel has run once before the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=s):
+        dev_round(torch.cuda.current_stream())
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(K):
+        g.replay()
+    host_graph = (time.perf_counter() - t_start) / K
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t_start) / K
+    # host cost of issuing the eager round (its launches queue behind each other)
+    n = 5
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(n):
+        eager_round(B, R)
+    host_eager = (time.perf_counter() - t_start) / n
+    torch.cuda.synchronize()
+    del g
+    return dict(ms_per_step=ms, host_us_graph=1e6 * host_graph, host_us_eager=1e6 * host_eager,
+                launches_per_round=len(R["layers"]) + 3)
+
+
 def inputs_layers():
     from streaming_diffusion_portrait_amd import inputs
     return inputs.SD15_LAYERS
@@ -157,73 +271,21 @@ def main():
         one_layer(args, B, todev, m, F, H)
         return
 
-    # ---- inputs: fresh seeded tensors per layer -------------------------------------------------
+    # ---- the round at the seeded m: inputs, eager timed region, captured graph ---------------
     t0 = time.perf_counter()
-    layers = []
-    for li, (name, L, C) in enumerate(inputs.SD15_LAYERS):
-        lay = inputs.attention_layer(1000 * SEED + li, F, L, C, m)
-        q = todev(lay["q"])
-        segs = [(todev(lay["k_self"]), todev(lay["v_self"]))]
-        segs += [(todev(k), todev(v)) for k, v in zip(lay["bank_k"], lay["bank_v"])]
-        out = torch.empty_like(q)
-        call = B.PreparedAttn(q, segs, H, out)
-        lk = L * (2 + m)
-        layers.append(dict(name=name, L=L, C=C, d=C // H, lk=lk, q=q, segs=segs, out=out, call=call,
-                           host=lay if li == 0 else None,
-                           flops=attention_flops(F, L, C, lk), bytes=attention_bytes(F, L, C, m)))
-    x_t_np, eps_np = inputs.ddim_pile(SEED, (16, 4, 64, 64))
-    x_t, eps = todev(x_t_np), todev(eps_np)
-    x_prev = torch.empty_like(x_t)
-    x0 = torch.empty((4, 4, 64, 64), dtype=torch.float32, device=dev)
-    n_bank = 1 + m
-    bank_np, q_np, _ = inputs.motion_bank(SEED, n_bank, 512, nq=1)
-    mb, mq = todev(bank_np), todev(q_np)
-    md = (torch.empty(1, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
-          torch.empty(1, dtype=torch.uint8, device=dev))
+    R = build_round(B, inputs, todev, m, F, H, dev)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t0:.1f}s (m={m})")
-
-    pile = B.Pile(4, 333)
-    next_window = [4]  # ids 0..2 prefilled, 3 enters with the first round
-
-    def step(events=None):
-        # the round's 16 attention layers, then the DDIM step (which also draws
-        # the next window's noise into the leaving window's slot) and the drift check
-        for li, lay in enumerate(layers):
-            if events is not None:
-                events[li][0].record()
-            lay["call"]()
-            if events is not None:
-                events[li][1].record()
-        _, t_slot, emit = pile.begin_round()
-        B.pyramid_ddim_step(x_t, eps, t_slot, x_prev=x_prev, x0_out=x0, emit_window=emit,
-                            roll=(SEED, next_window[0]))
-        next_window[0] += 1
-        pile.end_round()
-        B.motion_bank_min_l2(mq, mb, 17.0, out=md)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # ---- timed region: K whole rounds ----------------------------------------------------------
     K = args.steps
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in layers]
-           for _ in range(K)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for k in range(K):
-        step(evs[k])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    ms_per_step = 1e3 * elapsed / K
-
-    per_layer_ms = [float(np.mean([evs[k][li][0].elapsed_time(evs[k][li][1]) for k in range(K)]))
-                    for li in range(len(layers))]
+    ms_per_step, per_layer_ms = time_eager_rounds(R, args.warmup, K)
+    graph = time_graph_rounds(B, R, args.warmup, K)
+    layers = R["layers"]
     round_flops = sum(l["flops"] for l in layers)
     attn_ms = sum(per_layer_ms)
     tflops_round = round_flops / (ms_per_step * 1e-3) / 1e12
     frames_per_s = FRAMES_OUT_PER_ROUND / (ms_per_step * 1e-3)
+    log(f"  round m={m}: eager {ms_per_step:.3f} ms, graph {graph['ms_per_step']:.3f} ms; host issue per round: "
+        f"eager {graph['host_us_eager']:.0f} us, graph {graph['host_us_graph']:.0f} us")
 
     # dominant kernel: the d=40 (64^2 level) attention launches, 87% of the round's FLOPs at m=0
     dom = [li for li, l in enumerate(layers) if l["d"] == 40]
@@ -240,6 +302,35 @@ def main():
     for r in layer_report:
         log(f"  {r['layer']:>4} L={r['L']:5d} d={r['d']:3d} keys={r['keys']:5d}  {r['us']:9.2f} us  "
             f"{r['tflops']:7.1f} TFLOP/s  {r['pct_fp16_peak']:5.1f}%")
+    x_t, eps, x_prev, x0 = R["x_t"], R["eps"], R["x_prev"], R["x0"]
+    mb, mq, md = R["mb"], R["mq"], R["md"]
+    n_bank = 1 + m
+
+    # ---- the round at every anchor count m = 0..3 (fresh seeded tensors per m) ----------------
+    sweep_m = []
+    for mm in range(4):
+        if mm == m:
+            sm = dict(ms=ms_per_step, per_layer=per_layer_ms, graph_ms=graph["ms_per_step"], flops=round_flops)
+        else:
+            Rm = build_round(B, inputs, todev, mm, F, H, dev, keep_host=False)
+            mms, mpl = time_eager_rounds(Rm, args.warmup, K)
+            gm = time_graph_rounds(B, Rm, args.warmup, K)
+            sm = dict(ms=mms, per_layer=mpl, graph_ms=gm["ms_per_step"], flops=sum(l["flops"] for l in Rm["layers"]))
+            del Rm, gm
+            torch.cuda.synchronize()
+        d40 = float(np.mean([sm["per_layer"][li] for li in dom]))
+        rec = dict(m=mm, keys_64x64=4096 * (2 + mm), round_attn_tflop=round(sm["flops"] / 1e12, 4),
+                   ms_per_round=round(sm["ms"], 4), graph_ms_per_round=round(sm["graph_ms"], 4),
+                   tflops=round(sm["flops"] / (sm["ms"] * 1e-3) / 1e12, 1),
+                   pct_fp16_peak=round(100 * sm["flops"] / (sm["ms"] * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 2),
+                   frames_per_s=round(FRAMES_OUT_PER_ROUND / (sm["ms"] * 1e-3), 1),
+                   d40_us_per_launch=round(1e3 * d40, 1),
+                   d40_pct_fp16_peak=round(100 * (4 * 16 * 4096 * 4096 * (2 + mm) * 320) / (d40 * 1e-3) / 1e12
+                                           / PEAK_FP16_TFLOPS, 2))
+        sweep_m.append(rec)
+        log(f"  m={mm}: round {rec['ms_per_round']:.3f} ms (graph {rec['graph_ms_per_round']:.3f}), "
+            f"{rec['tflops']:.0f} TFLOP/s = {rec['pct_fp16_peak']:.1f}%, {rec['frames_per_s']:.0f} frames/s, "
+            f"d=40 {rec['d40_us_per_launch']:.0f} us ({rec['d40_pct_fp16_peak']:.1f}%)")
 
     # ---- DDIM and motion at the round's shapes (separately timed, same kernels) ---------------
     def time_it(fn, n=200):
@@ -381,6 +472,14 @@ def main():
             "algorithmic_bytes_per_launch": dom_l["bytes"],
             "avg_launch_us": round(1e3 * dom_ms, 2),
         },
+        "graph": {"ms_per_step": round(graph["ms_per_step"], 4),
+                  "frames_per_s": round(FRAMES_OUT_PER_ROUND / (graph["ms_per_step"] * 1e-3), 1),
+                  "host_us_per_round_graph": round(graph["host_us_graph"], 1),
+                  "host_us_per_round_eager": round(graph["host_us_eager"], 1),
+                  "launches_per_round": graph["launches_per_round"],
+                  "note": "the same round with the pile state on the device, captured once and replayed: "
+                          "one host call per round"},
+        "m_sweep": sweep_m,
         "ddim": {"us_at_round_shape": round(ddim_us, 2), "bytes_at_round_shape": 3407872,
                  "us_with_roll_at_round_shape": round(roll_us, 2), "sweep": sweep},
         "pile_prefill_us": round(prefill_us, 2),

@@ -33,12 +33,13 @@ extern "C" {
 #endif
 
 typedef int32_t pl_status;
+typedef struct pl_pile pl_pile;  /* the latents pile's state machine (defined below) */
 #define PL_OK 0            /* success */
 #define PL_EINVAL 1        /* invalid argument (null pointer, size or index out of range) */
 #define PL_EUNSUPPORTED 2  /* valid in principle but not implemented (head dim, alignment) */
 #define PL_EDEVICE 3       /* the HIP runtime reported an error at launch */
 
-#define PL_ABI_VERSION 3
+#define PL_ABI_VERSION 4
 #define PL_MAX_SEGMENTS 8       /* key segments per attention call: self + reference + anchors (5 used) */
 #define PL_MAX_WINDOWS 8        /* windows per pile (the pages use 4) */
 #define PL_MAX_MOTION_BANK 4    /* reference embedding + at most 3 anchors */
@@ -195,6 +196,51 @@ pl_status pl_pyramid_ddim_step_roll(const float* x_t, const float* eps, float* x
                                     uint64_t seed, uint64_t new_window_id, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * The round with its state on the device (one captured graph per stream)
+ *
+ * PersonaLive, section TensorRT 融合: bind() keeps the rolling latents and
+ * the pile's bookkeeping on the device so that a whole round is one host
+ * call.  Here the pile's integer state (a pl_pile, initialised with
+ * pl_pile_init and copied to device memory by the caller) is read and
+ * advanced by the kernels themselves, so the launches of a round take the
+ * same arguments every round and can be captured once in a HIP graph and
+ * replayed.
+ * ------------------------------------------------------------------------ */
+
+/* Host: write Stable Diffusion's scaled_linear alpha_bar table (betas from
+ * 0.00085 to 0.012 in sqrt space, fp64) into out[0..T-1]; T must be 1000.
+ * (The caller copies it to the device for pl_pyramid_ddim_step_device.) */
+pl_status pl_sd_alphas_cumprod(double* out, int32_t T);
+
+/* One round of the pile's device-side roll, driven by the device state:
+ *   1. the new window enters (as pl_pile_begin_round would place it: id
+ *      next_id, slot (head + count) % W, t = t_top);
+ *   2. the DDIM step of pl_pyramid_ddim_step_roll with each slot's timestep,
+ *      the leaving slot (the window at t = 0, if any) and the next window's
+ *      id (its noise, pl_window_noise(seed, id), fills the leaving slot of
+ *      x_prev) all read from the state; the coefficients are computed in
+ *      fp64 on the device from alphas_cumprod and rounded to fp32;
+ *   3. the state advances as pl_pile_end_round would leave it.
+ * Two kernel launches, no host synchronisation, no allocation and no memset.
+ *   x_t, eps, x_prev  device fp32 [W][elems_per_window] (x_prev may alias x_t),
+ *                 16-byte aligned; elems_per_window a multiple of 4.
+ *   x0_out        device fp32 [elems_per_window], 16-byte aligned: written in
+ *                 the rounds in which a window leaves.
+ *   W             2..PL_MAX_WINDOWS, equal to the W of the state.
+ *   pile          device pl_pile, 8-byte aligned, initialised by pl_pile_init
+ *                 (no round open); values read from it are clamped into range,
+ *                 so a corrupted state gives wrong results but no access out
+ *                 of bounds.
+ *   alphas_cumprod  device fp64 [T] (e.g. pl_sd_alphas_cumprod), 8-byte aligned.
+ *   final_alpha_cumprod  as pl_pyramid_ddim_step (negative: alphas_cumprod[0]).
+ * Errors: PL_EINVAL for null pointers or sizes out of range, PL_EUNSUPPORTED
+ * for misaligned buffers; nothing is launched then. */
+pl_status pl_pyramid_ddim_step_device(const float* x_t, const float* eps, float* x_prev, float* x0_out,
+                                      int32_t W, int64_t elems_per_window, pl_pile* pile,
+                                      const double* alphas_cumprod, int32_t T, double final_alpha_cumprod,
+                                      uint64_t seed, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Window noise, staircase prefill, first-frames interpolation
  *
  * PersonaLive, section 流式金字塔去噪: windows of pure noise enter the pile;
@@ -273,7 +319,7 @@ pl_status pl_motion_bank_min_l2(const float* query, int32_t nq, const float* ban
  * t_top, t_top - step_len, ..., 0 in consecutive rounds and is popped after
  * its t = 0 evaluation (t_top must be a multiple of step_len).
  * ------------------------------------------------------------------------ */
-typedef struct pl_pile {
+struct pl_pile {
   int32_t W;                       /* slots = windows per forward */
   int32_t step_len;                /* timestep decrement per round */
   int32_t t_top;                   /* timestep of a newly enqueued window */
@@ -283,7 +329,7 @@ typedef struct pl_pile {
   int32_t t[PL_MAX_WINDOWS];       /* timestep per slot (valid for held slots) */
   int64_t id[PL_MAX_WINDOWS];      /* window id per slot, -1 = free */
   int64_t next_id;                 /* id of the next enqueued window */
-} pl_pile;
+};
 
 /* Initialise.  W in 2..PL_MAX_WINDOWS, step_len >= 1, t_top = (W-1)*step_len.
  * prefill != 0 places W-1 windows at 0, step_len, ..., (W-2)*step_len in

@@ -32,6 +32,8 @@ EXPORTED = (
     "pl_refbank_attn",
     "pl_pyramid_ddim_step",
     "pl_pyramid_ddim_step_roll",
+    "pl_sd_alphas_cumprod",
+    "pl_pyramid_ddim_step_device",
     "pl_window_noise",
     "pl_pile_prefill",
     "pl_lerp_points",
@@ -107,6 +109,10 @@ def load():
     lib.pl_pyramid_ddim_step_roll.restype = i32
     lib.pl_pyramid_ddim_step_roll.argtypes = [vp, vp, vp, vp, i32, i64, ctypes.POINTER(i32), i32,
                                               ctypes.POINTER(f64), i32, f64, i32, u64, u64, vp]
+    lib.pl_sd_alphas_cumprod.restype = i32
+    lib.pl_sd_alphas_cumprod.argtypes = [ctypes.POINTER(f64), i32]
+    lib.pl_pyramid_ddim_step_device.restype = i32
+    lib.pl_pyramid_ddim_step_device.argtypes = [vp, vp, vp, vp, i32, i64, vp, vp, i32, f64, u64, vp]
     lib.pl_window_noise.restype = i32
     lib.pl_window_noise.argtypes = [vp, i64, u64, u64, vp]
     lib.pl_pile_prefill.restype = i32
@@ -156,6 +162,14 @@ def pl_pyramid_ddim_step(*args):
 
 def pl_pyramid_ddim_step_roll(*args):
     return load().pl_pyramid_ddim_step_roll(*args)
+
+
+def pl_sd_alphas_cumprod(*args):
+    return load().pl_sd_alphas_cumprod(*args)
+
+
+def pl_pyramid_ddim_step_device(*args):
+    return load().pl_pyramid_ddim_step_device(*args)
 
 
 def pl_window_noise(*args):
@@ -482,6 +496,54 @@ class Pile:
         return [self._p.id[s] for s in range(self.W)]
 
 
+def sd_alphas_cumprod():
+    """The library's built-in alpha_bar table (SD scaled_linear, T = 1000) as a host list."""
+    ab = (ctypes.c_double * 1000)()
+    _check("pl_sd_alphas_cumprod", pl_sd_alphas_cumprod(ab, 1000))
+    return list(ab)
+
+
+class DevicePile:
+    """The pile's state machine held in device memory (see ``pl_pyramid_ddim_step_device``).
+
+    The state starts as ``pl_pile_init`` leaves it and is read and advanced by
+    the kernels, so ``step`` issues the same launches every round -- a round
+    built from it can be captured once in a graph and replayed.  ``state()``
+    copies the state back to the host (a synchronising read).
+    """
+
+    def __init__(self, W=4, step_len=333, prefill=True, device="cuda", alphas_cumprod=None):
+        host = pl_pile()
+        _check("pl_pile_init", pl_pile_init(ctypes.byref(host), W, step_len, (W - 1) * step_len,
+                                            1 if prefill else 0))
+        raw = torch.frombuffer(bytearray(bytes(host)), dtype=torch.uint8)
+        self.buf = raw.to(device)  # 8-byte aligned device allocation
+        ab = sd_alphas_cumprod() if alphas_cumprod is None else [float(a) for a in alphas_cumprod]
+        self.ab = torch.tensor(ab, dtype=torch.float64, device=device)
+        self.W = W
+
+    def step(self, x_t, eps, x_prev, x0_out, seed, final_alpha_cumprod=-1.0, stream=None):
+        """One round: the new window enters, the rolling DDIM step, the state advances."""
+        for t, name in ((x_t, "x_t"), (eps, "eps"), (x_prev, "x_prev"), (x0_out, "x0_out")):
+            _need(t, torch.float32, name)
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        if x_t.numel() != eps.numel() or x_prev.numel() != x_t.numel() or x_t.numel() % self.W:
+            raise ValueError("x_t, eps and x_prev must hold W equal windows")
+        per = x_t.numel() // self.W
+        if x0_out.numel() != per:
+            raise ValueError("x0_out must hold one window")
+        _check("pl_pyramid_ddim_step_device",
+               pl_pyramid_ddim_step_device(ctypes.c_void_p(x_t.data_ptr()), ctypes.c_void_p(eps.data_ptr()),
+                                           ctypes.c_void_p(x_prev.data_ptr()), ctypes.c_void_p(x0_out.data_ptr()),
+                                           self.W, per, ctypes.c_void_p(self.buf.data_ptr()),
+                                           ctypes.c_void_p(self.ab.data_ptr()), self.ab.numel(),
+                                           float(final_alpha_cumprod), int(seed), _stream_ptr(stream)))
+
+    def state(self):
+        return pl_pile.from_buffer_copy(self.buf.cpu().numpy().tobytes())
+
+
 class PreparedAttn:
     """A pl_refbank_attn call with its arguments marshalled once.
 
@@ -515,7 +577,9 @@ class PreparedAttn:
         self.flops = 4 * F * L * sum(s.len for s in self._segs) * C
         self._fn = load().pl_refbank_attn
 
-    def __call__(self):
-        st = self._fn(*self.args)
+    def __call__(self, stream=None):
+        """Launch; ``stream`` (e.g. a graph's capture stream) overrides the prepared one."""
+        args = self.args if stream is None else self.args[:-1] + (_stream_ptr(stream),)
+        st = self._fn(*args)
         if st != PL_OK:
             raise PlError("pl_refbank_attn", st, last_error())

@@ -259,6 +259,44 @@ pl_status pl_pyramid_ddim_step_roll(const float* x_t, const float* eps, float* x
                         final_alpha_cumprod, emit_window, 1, seed, new_window_id, stream);
 }
 
+pl_status pl_sd_alphas_cumprod(double* out, int32_t T) {
+  if (!out) return fail(PL_EINVAL, "pl_sd_alphas_cumprod: out must be non-null");
+  if (T != 1000) return fail(PL_EINVAL, "pl_sd_alphas_cumprod: the built-in schedule has T = 1000 (got %d)", T);
+  std::memcpy(out, sd_schedule().ab, sizeof(double) * 1000);
+  return ok();
+}
+
+pl_status pl_pyramid_ddim_step_device(const float* x_t, const float* eps, float* x_prev, float* x0_out, int32_t W,
+                                      int64_t elems_per_window, pl_pile* pile, const double* alphas_cumprod, int32_t T,
+                                      double final_alpha_cumprod, uint64_t seed, void* stream) {
+  const char* fn = "pl_pyramid_ddim_step_device";
+  if (!x_t || !eps || !x_prev || !x0_out) return fail(PL_EINVAL, "%s: x_t, eps, x_prev and x0_out must be non-null", fn);
+  if (!pile || !alphas_cumprod) return fail(PL_EINVAL, "%s: pile and alphas_cumprod must be non-null", fn);
+  if (W < 2 || W > PL_MAX_WINDOWS) return fail(PL_EINVAL, "%s: W must be in [2, %d] (got %d)", fn, PL_MAX_WINDOWS, W);
+  if (elems_per_window < 1 || elems_per_window > (int64_t(1) << 40))
+    return fail(PL_EINVAL, "%s: elems_per_window must be in [1, 2^40]", fn);
+  if (T < 1) return fail(PL_EINVAL, "%s: T must be >= 1", fn);
+  if (!(final_alpha_cumprod < 0.0 || (final_alpha_cumprod > 0.0 && final_alpha_cumprod <= 1.0)))
+    return fail(PL_EINVAL, "%s: final_alpha_cumprod must be negative (alpha_bar[0]) or in (0, 1]", fn);
+  if (elems_per_window % 4 || !aligned16(x_t) || !aligned16(eps) || !aligned16(x_prev) || !aligned16(x0_out))
+    return fail(PL_EUNSUPPORTED, "%s: buffers must be 16-byte aligned and elems_per_window a multiple of 4", fn);
+  if ((reinterpret_cast<uintptr_t>(pile) & 7) || (reinterpret_cast<uintptr_t>(alphas_cumprod) & 7))
+    return fail(PL_EUNSUPPORTED, "%s: pile and alphas_cumprod must be 8-byte aligned", fn);
+  pl::DeviceRoundLaunch a;
+  a.x_t = x_t;
+  a.eps = eps;
+  a.x_prev = x_prev;
+  a.x0_out = x0_out;
+  a.W = W;
+  a.elems_per_window = elems_per_window;
+  a.pile = pile;
+  a.alphas_cumprod = alphas_cumprod;
+  a.T = T;
+  a.final_alpha_cumprod = final_alpha_cumprod;
+  a.seed = seed;
+  return device_status(pl::launch_pyramid_round_device(a, static_cast<hipStream_t>(stream)), "pl_pyramid_ddim_step_device launch");
+}
+
 // ---------------------------------------------------------------------------
 pl_status pl_window_noise(float* out, int64_t n, uint64_t seed, uint64_t window_id, void* stream) {
   if (!out) return fail(PL_EINVAL, "pl_window_noise: out must be non-null");

@@ -50,6 +50,25 @@ struct DdimLaunch {
 
 hipError_t launch_pyramid_ddim(const DdimLaunch& a, hipStream_t stream);
 
+// The rolling step driven by a device-resident pile state, then the state's
+// advance (two launches).  Requires 16-byte aligned buffers and
+// elems_per_window % 4 == 0.
+struct DeviceRoundLaunch {
+  const float* x_t;
+  const float* eps;
+  float* x_prev;
+  float* x0_out;
+  int32_t W;
+  int64_t elems_per_window;
+  pl_pile* pile;                 // device
+  const double* alphas_cumprod;  // device [T]
+  int32_t T;
+  double final_alpha_cumprod;
+  uint64_t seed;
+};
+
+hipError_t launch_pyramid_round_device(const DeviceRoundLaunch& a, hipStream_t stream);
+
 // ---- pile roll: window noise, staircase prefill, interpolation -----------------
 struct NoiseLaunch {
   const float* ref;    // nullptr: pure noise

@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pl_abi_version() == 3
+    assert lib.pl_abi_version() == 4
     assert [B.status_name(s) for s in range(4)] == ["PL_OK", "PL_EINVAL", "PL_EUNSUPPORTED", "PL_EDEVICE"]
     assert B.status_name(99) == "PL_UNKNOWN"
 
@@ -260,3 +260,31 @@ def test_pile_matches_oracle_queue(lib, prefill, pages_constants):
         else:
             assert emit_slot == slot_of[emitted] and t_slot[emit_slot] == 0
         assert pile.end_round() == (-1 if emitted is None else emitted)
+
+
+def test_sd_alphas_cumprod_table(lib):
+    # the library's built-in schedule, read back through the ABI, is the oracle's
+    import numpy as np
+    from oracle import sd_scaled_linear_alphas_cumprod
+    ab = (ctypes.c_double * 1000)()
+    assert lib.pl_sd_alphas_cumprod(ab, 1000) == B.PL_OK
+    assert np.max(np.abs(np.array(ab) - sd_scaled_linear_alphas_cumprod())) <= 1e-15
+    assert lib.pl_sd_alphas_cumprod(ab, 999) == B.PL_EINVAL
+    assert lib.pl_sd_alphas_cumprod(None, 1000) == B.PL_EINVAL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), B.PL_EINVAL), (dict(x0=None), B.PL_EINVAL), (dict(pile=None), B.PL_EINVAL),
+    (dict(ab=None), B.PL_EINVAL), (dict(W=1), B.PL_EINVAL), (dict(W=9), B.PL_EINVAL), (dict(n=0), B.PL_EINVAL),
+    (dict(T=0), B.PL_EINVAL), (dict(fin=1.5), B.PL_EINVAL), (dict(fin=0.0), B.PL_EINVAL),
+    (dict(n=258), B.PL_EUNSUPPORTED), (dict(x=MIS), B.PL_EUNSUPPORTED), (dict(x0=MIS), B.PL_EUNSUPPORTED),
+    (dict(pile=ctypes.c_void_p(0x30004)), B.PL_EUNSUPPORTED),
+])
+def test_ddim_device_rejects(lib, kw, status):
+    a = dict(x=A, e=A2, xp=A, x0=A2, W=4, n=256, pile=ctypes.c_void_p(0x30000), ab=ctypes.c_void_p(0x40000),
+             T=1000, fin=-1.0)
+    a.update(kw)
+    st = B.pl_pyramid_ddim_step_device(a["x"], a["e"], a["xp"], a["x0"], a["W"], a["n"], a["pile"], a["ab"], a["T"],
+                                       a["fin"], 7, None)
+    assert st == status
+    assert B.last_error() != ""
