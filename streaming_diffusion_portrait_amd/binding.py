@@ -261,11 +261,37 @@ def make_segments(segments, frames=None, channels=None):
     return arr, segments
 
 
-def refbank_attn(q, segments, heads, out=None, scale=None, stream=None):
+def _workspace(F, L, heads, d, segs, device, workspace=None):
+    """(pointer, bytes) of the key-split workspace the call needs: ``workspace``
+    (a device tensor) if given, else a fresh allocation; (None, 0) when the
+    launch splits nothing."""
+    if workspace is False:  # run the single-pass kernels
+        return None, 0, None
+    lens = (ctypes.c_int64 * len(segs))(*[s.len for s in segs])
+    need = load().pl_refbank_attn_workspace_size(F, L, heads, d, lens, len(segs))
+    if workspace is None:
+        if not need:
+            return None, 0, None
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous device tensor")
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), workspace
+
+
+def workspace_size(F, L, heads, d, seg_lens):
+    """Bytes of workspace ``pl_refbank_attn`` needs for these sizes (0: none)."""
+    lens = (ctypes.c_int64 * len(seg_lens))(*[int(x) for x in seg_lens])
+    return int(load().pl_refbank_attn_workspace_size(F, L, heads, d, lens, len(seg_lens)))
+
+
+def refbank_attn(q, segments, heads, out=None, scale=None, stream=None, workspace=None):
     """O = ref-bank attention of one layer (see ``pl_refbank_attn``).
 
     ``q``: fp16 device ``[F, L, C]``; ``segments`` as for :func:`make_segments`;
-    ``heads``: H with d = C / H.  Returns ``out`` (allocated if None).
+    ``heads``: H with d = C / H.  ``workspace``: a device tensor of at least
+    :func:`workspace_size` bytes for the launches that split the key axis
+    (allocated here when needed and not given; ``False`` runs the single-pass
+    kernels instead).  Returns ``out`` (allocated if None).
     """
     _need(q, torch.float16, "q")
     if q.dim() != 3:
@@ -284,12 +310,9 @@ def refbank_attn(q, segments, heads, out=None, scale=None, stream=None):
     q_ld, q_fs = _rows(q, "q")
     o_ld, o_fs = _rows(out, "out")
     segs, _keep = make_segments(segments, F, C)
-    lens = (ctypes.c_int64 * len(segments))(*[s.len for s in segs])
-    ws = load().pl_refbank_attn_workspace_size(F, L, heads, d, lens, len(segments))
-    if ws:
-        raise RuntimeError("workspace-requiring configuration is not expected here")
+    ws, ws_bytes, _ws_keep = _workspace(F, L, heads, d, segs, q.device, workspace)
     st = pl_refbank_attn(ctypes.c_void_p(q.data_ptr()), q_ld, q_fs, ctypes.c_void_p(out.data_ptr()), o_ld, o_fs,
-                         F, L, heads, d, segs, len(segments), float(scale), None, 0, _stream_ptr(stream))
+                         F, L, heads, d, segs, len(segments), float(scale), ws, ws_bytes, _stream_ptr(stream))
     _check("pl_refbank_attn", st)
     return out
 
@@ -551,10 +574,13 @@ class PreparedAttn:
     the object only crosses into the library (one ctypes call), so per-launch
     host cost stays far below the small layers' GPU time.  The tensors must
     stay alive and unchanged in shape while the object is used; ``stream``
-    is fixed at preparation (default: the current stream then).
+    is fixed at preparation (default: the current stream then).  A launch
+    that splits the key axis keeps its workspace (``workspace``, or one
+    allocated here) for the object's lifetime; calls on one workspace must
+    not overlap in time.
     """
 
-    def __init__(self, q, segments, heads, out, scale=None, stream=None):
+    def __init__(self, q, segments, heads, out, scale=None, stream=None, workspace=None):
         _need(q, torch.float16, "q")
         _need(out, torch.float16, "out")
         if q.dim() != 3 or out.shape != q.shape:
@@ -568,12 +594,11 @@ class PreparedAttn:
         q_ld, q_fs = _rows(q, "q")
         o_ld, o_fs = _rows(out, "out")
         self._segs, self._keep = make_segments(segments, F, C)
+        ws, ws_bytes, self._ws = _workspace(F, L, heads, d, self._segs, q.device, workspace)
         self._tensors = (q, out)
-        lens = (ctypes.c_int64 * len(segments))(*[s.len for s in self._segs])
-        if load().pl_refbank_attn_workspace_size(F, L, heads, d, lens, len(segments)):
-            raise RuntimeError("workspace-requiring configuration is not expected here")
+        self.workspace_bytes = ws_bytes
         self.args = (ctypes.c_void_p(q.data_ptr()), q_ld, q_fs, ctypes.c_void_p(out.data_ptr()), o_ld, o_fs,
-                     F, L, heads, d, self._segs, len(segments), float(scale), None, 0, _stream_ptr(stream))
+                     F, L, heads, d, self._segs, len(segments), float(scale), ws, ws_bytes, _stream_ptr(stream))
         self.flops = 4 * F * L * sum(s.len for s in self._segs) * C
         self._fn = load().pl_refbank_attn
 

@@ -149,7 +149,7 @@ struct Cfg {
   static_assert(BN == 64, "one plane per load instruction: 64 keys of 16 bytes");
   static_assert(PLB % 16 == 0, "planes hold 16-byte chunks");
   static_assert(NBUF >= 2 && NBUF <= 6, "ring of 2 to 6 buffers");
-  static_assert(NI * (NBUF - 1) <= 24, "vmcnt wait table range");
+  static_assert(NI * (NBUF - 1) <= 48, "vmcnt wait table range");
   static_assert(!PV32 || ONES, "32-row PV tiles take the row sums from the ones row at dim D of the padding");
   static_assert(!PV32 || NRT <= 3, "lane offsets for up to three 32-row O^T tiles");
 };
@@ -161,6 +161,12 @@ struct KParams {
   int F, Lq, H, nqt, nseg;
   float c2;  // scale * log2(e)
   AttnSegment seg[PL_MAX_SEGMENTS];
+  // key-axis split: nsplit workgroups per (head, frame, query tile), split s
+  // taking key tiles [s*tps, (s+1)*tps); with nsplit > 1 the kernel writes
+  // per-split partials (unnormalised O, offset, row sum) instead of O
+  int nsplit, tps;
+  float* part_o;  // [F*H*nsplit][Lq][D] fp32
+  float* part_ml; // [F*H*nsplit][Lq][2] fp32: offset (log2 units), row sum
 };
 
 __device__ __forceinline__ unsigned pack_h2(float a, float b) {
@@ -188,8 +194,12 @@ __device__ __forceinline__ void wait_vm(int n) {
     PL_VMCNT_CASE(7) PL_VMCNT_CASE(8) PL_VMCNT_CASE(9) PL_VMCNT_CASE(10) PL_VMCNT_CASE(11) PL_VMCNT_CASE(12)
     PL_VMCNT_CASE(13) PL_VMCNT_CASE(14) PL_VMCNT_CASE(15) PL_VMCNT_CASE(16) PL_VMCNT_CASE(17) PL_VMCNT_CASE(18)
     PL_VMCNT_CASE(19) PL_VMCNT_CASE(20) PL_VMCNT_CASE(21) PL_VMCNT_CASE(22) PL_VMCNT_CASE(23) PL_VMCNT_CASE(24)
+    PL_VMCNT_CASE(25) PL_VMCNT_CASE(26) PL_VMCNT_CASE(27) PL_VMCNT_CASE(28) PL_VMCNT_CASE(29) PL_VMCNT_CASE(30)
+    PL_VMCNT_CASE(31) PL_VMCNT_CASE(32) PL_VMCNT_CASE(33) PL_VMCNT_CASE(34) PL_VMCNT_CASE(35) PL_VMCNT_CASE(36)
+    PL_VMCNT_CASE(37) PL_VMCNT_CASE(38) PL_VMCNT_CASE(39) PL_VMCNT_CASE(40) PL_VMCNT_CASE(41) PL_VMCNT_CASE(42)
+    PL_VMCNT_CASE(43) PL_VMCNT_CASE(44) PL_VMCNT_CASE(45) PL_VMCNT_CASE(46) PL_VMCNT_CASE(47) PL_VMCNT_CASE(48)
     default:
-      if (n > 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+      if (n > 48) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       break;
   }
@@ -866,10 +876,12 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
   lc.g = lc.lane >> 4;
   const int c32 = lc.lane & 31;
 
-  // XCD-aware remap of the workgroup id onto (head, frame, query tile).
-  const int total = p.nqt * p.F * p.H;
+  // XCD-aware remap of the workgroup id onto (head, frame, query tile, split).
+  const int total = p.nqt * p.F * p.H * p.nsplit;
   int lid = blockIdx.x;
   if ((total & 7) == 0) lid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int split = lid % p.nsplit;
+  lid /= p.nsplit;
   const int hd = lid / (p.F * p.nqt);
   const int rem = lid - hd * (p.F * p.nqt);
   const int f = rem / p.nqt;
@@ -933,12 +945,25 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
       }
   }
 
-  // Tiles in the key sequence and this wave's copy instructions per tile.
+  // Tiles in the key sequence (this split's range of them) and this wave's
+  // copy instructions per tile.
   int ntiles = 0;
   bool full = true;  // every tile holds BN real keys: no masking anywhere
   for (int s = 0; s < p.nseg; ++s) {
     ntiles += (int)((p.seg[s].len + C::BN - 1) / C::BN);
     full &= (p.seg[s].len % C::BN) == 0;
+  }
+  const int t_begin = min(split * p.tps, ntiles);
+  ntiles = min(ntiles, t_begin + p.tps) - t_begin;
+  int s0 = 0;  // segment and key offset of the split's first tile
+  int64_t off0 = 0;
+  for (int t = t_begin; s0 < p.nseg; ++s0) {
+    const int nts = (int)((p.seg[s0].len + C::BN - 1) / C::BN);
+    if (t < nts) {
+      off0 = (int64_t)t * C::BN;
+      break;
+    }
+    t -= nts;
   }
   Copier<C> cp;
   cp.ni = 0;
@@ -976,14 +1001,14 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
       if constexpr (C::ONES) if (lc.h) ws.qf[qb][C::KST - 1][0] = (_Float16)0.0f;  // offset column: none yet
     }
 
-    cp.s = 0;
-    cp.off = 0;
+    cp.s = s0;
+    cp.off = off0;
     cp.issued = 0;
     while (cp.issued < C::NBUF - 1 && cp.issued < ntiles) issue_tile<C>(p, smem, cp, f, hd, wave, lc.lane);
 
     // ---- tile 0: exact ----
-    int cs = 0;  // segment / offset of the tile being consumed
-    int64_t coff = 0;
+    int cs = s0;  // segment / offset of the tile being consumed
+    int64_t coff = off0;
     wait_vm(cp.ni * (cp.issued - 1));  // tile 0 has landed
     __syncthreads();
     if (cp.issued < ntiles) issue_tile<C>(p, smem, cp, f, hd, wave, lc.lane);  // ring slot NBUF-1 is still unused
@@ -1131,7 +1156,43 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
     for (int w = 0; w < C::W; ++w) any_bad |= flags[w];
     return __builtin_amdgcn_readfirstlane(any_bad) != 0;
   };
-  if (pass(std::false_type{})) pass(std::true_type{});
+  if (ntiles > 0 && pass(std::false_type{})) pass(std::true_type{});
+
+  if (p.nsplit > 1) {
+    // ---- this split's partials: unnormalised O^T, offset and row sum per query ----
+    static_assert(!C::PV32, "key splits are dispatched for the 16-row PV layout only");
+    const int64_t pbase = ((int64_t)(f * p.H + hd) * p.nsplit + split) * p.Lq;
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) {
+#pragma unroll
+      for (int grp = 0; grp < 2; ++grp) {
+        float l;
+        if constexpr (C::ONES) {
+          constexpr int tl = C::D / 16, gl = (C::D % 16) / 4, rl = C::D % 4;
+          l = __shfl(ws.oacc[qb][grp][tl][rl], 16 * gl + lc.c16, 64);
+        } else {
+          l = __shfl(ws.osum[qb][grp][0], lc.c16, 64);  // row 0: lanes 0..15
+        }
+        const float mo = __shfl(ws.mrun[qb], 16 * grp + lc.c16, 64);  // S layout: lane l%32 is query l%32
+        const int row = qrow0 + 32 * qb + 16 * grp + lc.c16;
+        if (row < p.Lq) {
+          const bool empty = ntiles <= 0;
+          float* po = p.part_o + (pbase + row) * C::D;
+#pragma unroll
+          for (int t = 0; t < C::NDT; ++t) {
+            const int col = 16 * t + 4 * lc.g;
+            if (col < C::D) *reinterpret_cast<f4*>(po + col) = empty ? (f4){0.f, 0.f, 0.f, 0.f} : ws.oacc[qb][grp][t];
+          }
+          if (lc.g == 0) {
+            float* pm = p.part_ml + (pbase + row) * 2;
+            pm[0] = empty ? -INFINITY : mo;
+            pm[1] = empty ? 0.f : l;
+          }
+        }
+      }
+    }
+    return;
+  }
 
   // ---- normalise and write O (fp16, round to nearest even) ----
   _Float16* ob = p.o + (int64_t)f * p.o_fs + (int64_t)hd * C::D;
@@ -1388,20 +1449,134 @@ hipError_t launch_short(const KParams& kp, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Merge the key splits of every query row: with M the largest split offset,
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, rounded to fp16.  One
+// thread per 4 output columns, columns fastest, so partial reads and output
+// stores are contiguous.
+template <int D>
+__global__ void __launch_bounds__(256) split_combine_kernel(const float* __restrict__ part_o,
+                                                            const float* __restrict__ part_ml, _Float16* o,
+                                                            int64_t o_ld, int64_t o_fs, int F, int H, int Lq,
+                                                            int nsplit) {
+  constexpr int Q = D / 4;
+  const int64_t total = (int64_t)F * H * Lq * Q;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int qd = (int)(i % Q);
+    int64_t rest = i / Q;
+    const int row = (int)(rest % Lq);
+    rest /= Lq;
+    const int hd = (int)(rest % H);
+    const int f = (int)(rest / H);
+    const int64_t pb = (int64_t)(f * H + hd) * nsplit * Lq + row;  // split s at pb + s * Lq
+    float M = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, part_ml[(pb + (int64_t)sp * Lq) * 2]);
+    float L = 0.f;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const int64_t r = pb + (int64_t)sp * Lq;
+      const float w = __builtin_amdgcn_exp2f(part_ml[r * 2] - M);
+      L = fmaf(w, part_ml[r * 2 + 1], L);
+      const f4 x = *reinterpret_cast<const f4*>(part_o + r * D + 4 * qd);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = fmaf(w, x[k], acc[k]);
+    }
+    const float inv = 1.0f / L;
+    h4 out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = (_Float16)(acc[k] * inv);
+    *reinterpret_cast<h4*>(o + (int64_t)f * o_fs + (int64_t)row * o_ld + (int64_t)hd * D + 4 * qd) = out;
+  }
+}
+
+// Workgroups of one launch: query tiles x frames x heads (x key splits).
+template <class C>
+int64_t attn_workgroups(int F, int Lq, int H) {
+  return (int64_t)((Lq + C::QWG - 1) / C::QWG) * F * H;
+}
+
+#ifndef PL_SPLIT_TARGET_WGS
+#define PL_SPLIT_TARGET_WGS 256  // d = 160 workgroups the GPU holds at once (one per CU: LDS)
+#endif
+#ifndef PL_SPLIT_MIN_TILES
+#define PL_SPLIT_MIN_TILES 8  // key tiles a split must keep to win back its partials' write and merge
+#endif
+
+// How many key splits a launch takes (and the tiles per split): only for the
+// head dim whose workgroups take a whole CU each (d = 160, the 16^2 and 8^2
+// levels: a 127.5 KB copy ring, one wave per SIMD), only as far as the launch
+// leaves CUs idle -- more workgroups than CUs would run in a second
+// generation and lose what the split gains -- and only with at least
+// PL_SPLIT_MIN_TILES tiles per split: a workgroup's fixed cost (its first
+// loads, the exact first tile) is several tiles' worth, and the partials'
+// round trip costs about five (measured: the 8^2 level's 5 tiles in two
+// splits took 23.5 us against 20.1 us in one pass).
+template <class C>
+void split_plan(int F, int Lq, int H, const int64_t* seg_len, int nseg, int& nsplit, int& tps) {
+  int ntiles = 0;
+  for (int s = 0; s < nseg; ++s) ntiles += (int)((seg_len[s] + C::BN - 1) / C::BN);
+  nsplit = 1;
+  tps = 1 << 30;
+  if (C::D != 160 || ntiles < 2) return;
+  const int64_t wgs = attn_workgroups<C>(F, Lq, H);
+  if (2 * wgs > PL_SPLIT_TARGET_WGS) return;
+  const int want = (int)std::min<int64_t>(ntiles / PL_SPLIT_MIN_TILES, PL_SPLIT_TARGET_WGS / wgs);
+  if (want < 2) return;
+  tps = (ntiles + want - 1) / want;
+  nsplit = (ntiles + tps - 1) / tps;
+  if (nsplit < 2) {
+    nsplit = 1;
+    tps = 1 << 30;
+  }
+}
+
 template <int D, int NQB, int NKB, int NBUF, int MINB, bool PIPE, int W, bool PV32 = false>
-hipError_t launch_cfg(const KParams& kp, hipStream_t stream) {
+hipError_t launch_cfg(const KParams& kp, hipStream_t stream, float* workspace) {
   using C = Cfg<D, NQB, NKB, NBUF, MINB, PIPE, W, PV32>;
   KParams p = kp;
   for (int i = 0; i < p.nseg; ++i)
     if (p.seg[i].ld * 2 * C::BN > 0x7fffffffLL) return hipErrorInvalidValue;  // 32-bit copy offsets
   p.nqt = (p.Lq + C::QWG - 1) / C::QWG;
-  const int64_t blocks = (int64_t)p.nqt * p.F * p.H;
+  p.nsplit = 1;
+  p.tps = 1 << 30;
+  p.part_o = p.part_ml = nullptr;
+  if (workspace) {
+    int64_t lens[PL_MAX_SEGMENTS];
+    for (int i = 0; i < p.nseg; ++i) lens[i] = p.seg[i].len;
+    split_plan<C>(p.F, p.Lq, p.H, lens, p.nseg, p.nsplit, p.tps);
+    if (p.nsplit > 1) {
+      p.part_o = workspace;
+      p.part_ml = workspace + (int64_t)p.F * p.H * p.nsplit * p.Lq * D;
+    }
+  }
+  const int64_t blocks = (int64_t)p.nqt * p.F * p.H * p.nsplit;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(refbank_attn_kernel<C>, dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, p);
+  if (p.nsplit == 1) return hipGetLastError();
+  if (hipError_t e = hipGetLastError()) return e;
+  const int64_t items = (int64_t)p.F * p.H * p.Lq * (D / 4);
+  const int64_t cblocks = std::min<int64_t>((items + 255) / 256, 4096);
+  hipLaunchKernelGGL(split_combine_kernel<D>, dim3((unsigned)cblocks), dim3(256), 0, stream, p.part_o, p.part_ml,
+                     p.o, p.o_ld, p.o_fs, p.F, p.H, p.Lq, p.nsplit);
   return hipGetLastError();
 }
 
+// d = 160 configurations: 4 waves of 32 query rows, or 2 for frames of at most 64 rows
+using Cfg160 = Cfg<160, 1, 2, 3, 1, false, 4>;
+using Cfg160s = Cfg<160, 1, 2, 3, 1, false, 2>;
+
 }  // namespace
+
+size_t refbank_attn_workspace_bytes(int32_t F, int32_t Lq, int32_t H, int32_t d, const int64_t* seg_len,
+                                    int32_t nseg) {
+  if (d != 160 || (nseg == 1 && seg_len[0] <= 64)) return 0;  // no split for the other kernels
+  int nsplit, tps;
+  if (Lq <= 64)
+    split_plan<Cfg160s>(F, Lq, H, seg_len, nseg, nsplit, tps);
+  else
+    split_plan<Cfg160>(F, Lq, H, seg_len, nseg, nsplit, tps);
+  if (nsplit < 2) return 0;
+  return (size_t)F * H * nsplit * Lq * (d + 2) * sizeof(float);
+}
 
 hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream) {
   KParams p;
@@ -1418,6 +1593,10 @@ hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream) {
   p.nseg = a.nseg;
   p.c2 = a.scale * kLog2e;
   for (int i = 0; i < PL_MAX_SEGMENTS; ++i) p.seg[i] = a.seg[i];
+  p.nsplit = 1;
+  p.tps = 1 << 30;
+  p.part_o = p.part_ml = nullptr;
+  float* ws = static_cast<float*>(a.workspace);
   // a single segment of at most one tile: the short-context kernel
   if (a.nseg == 1 && a.seg[0].len <= 64) {
     p.nqt = 0;
@@ -1430,14 +1609,16 @@ hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream) {
     }
   }
   switch (a.d) {
-    case 32: return launch_cfg<32, 2, 2, 4, 2, true, 4>(p, stream);
+    case 32: return launch_cfg<32, 2, 2, 4, 2, true, 4>(p, stream, nullptr);
 #if PL_D40_PV32
-    case 40: return launch_cfg<40, 2, 2, 4, 2, true, 4, true>(p, stream);
+    case 40: return launch_cfg<40, 2, 2, 4, 2, true, 4, true>(p, stream, nullptr);
 #else
-    case 40: return launch_cfg<40, 2, 2, 4, 2, true, 4>(p, stream);
+    case 40: return launch_cfg<40, 2, 2, 4, 2, true, 4>(p, stream, nullptr);
 #endif
-    case 80: return launch_cfg<80, 1, 2, 4, 1, true, 8>(p, stream);
-    case 160: return launch_cfg<160, 1, 2, 3, 1, false, 4>(p, stream);
+    case 80: return launch_cfg<80, 1, 2, 4, 1, true, 8>(p, stream, nullptr);
+    case 160:
+      if (a.Lq <= 64) return launch_cfg<160, 1, 2, 3, 1, false, 2>(p, stream, ws);
+      return launch_cfg<160, 1, 2, 3, 1, false, 4>(p, stream, ws);
     default: return hipErrorInvalidValue;
   }
 }

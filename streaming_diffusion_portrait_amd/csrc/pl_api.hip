@@ -169,16 +169,17 @@ const char* pl_last_error(void) { return g_last_error; }
 // ---------------------------------------------------------------------------
 size_t pl_refbank_attn_workspace_size(int32_t F, int32_t Lq, int32_t H, int32_t d, const int64_t* seg_len,
                                       int32_t nseg) {
-  (void)F; (void)Lq; (void)H; (void)d; (void)seg_len; (void)nseg;
-  return 0;
+  if (!seg_len || F < 1 || Lq < 1 || H < 1 || nseg < 1 || nseg > PL_MAX_SEGMENTS) return 0;
+  if (d != 32 && d != 40 && d != 80 && d != 160) return 0;
+  for (int i = 0; i < nseg; ++i)
+    if (seg_len[i] < 1) return 0;
+  return pl::refbank_attn_workspace_bytes(F, Lq, H, d, seg_len, nseg);
 }
 
 pl_status pl_refbank_attn(const void* q, int64_t q_ld, int64_t q_frame_stride, void* o, int64_t o_ld,
                           int64_t o_frame_stride, int32_t F, int32_t Lq, int32_t H, int32_t d,
                           const pl_kv_segment* segs, int32_t nseg, float scale, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!q || !o) return fail(PL_EINVAL, "pl_refbank_attn: q and o must be non-null");
   if (!segs) return fail(PL_EINVAL, "pl_refbank_attn: segs must be non-null");
   if (F < 1 || Lq < 1 || H < 1) return fail(PL_EINVAL, "pl_refbank_attn: F, Lq, H must be >= 1 (got %d, %d, %d)", F, Lq, H);
@@ -227,6 +228,19 @@ pl_status pl_refbank_attn(const void* q, int64_t q_ld, int64_t q_frame_stride, v
       return fail(PL_EINVAL, "pl_refbank_attn: o overlaps the keys or values of segment %d", i);
   }
   if (total > (int64_t(1) << 24)) return fail(PL_EINVAL, "pl_refbank_attn: total key length exceeds 2^24");
+  // workspace: the key-split partials where the launch splits the key axis;
+  // NULL with 0 bytes runs the single-pass kernels
+  int64_t lens[PL_MAX_SEGMENTS];
+  for (int i = 0; i < nseg; ++i) lens[i] = segs[i].len;
+  const size_t need = pl::refbank_attn_workspace_bytes(F, Lq, H, d, lens, nseg);
+  a.workspace = nullptr;
+  if (workspace || workspace_bytes) {
+    if (!workspace) return fail(PL_EINVAL, "pl_refbank_attn: workspace_bytes is %zu but workspace is NULL", workspace_bytes);
+    if (workspace_bytes < need)
+      return fail(PL_EINVAL, "pl_refbank_attn: workspace of %zu bytes is too small (%zu needed)", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(PL_EUNSUPPORTED, "pl_refbank_attn: workspace must be 16-byte aligned");
+    if (need > 0) a.workspace = workspace;
+  }
   a.q = static_cast<const _Float16*>(q);
   a.o = static_cast<_Float16*>(o);
   a.q_ld = q_ld;

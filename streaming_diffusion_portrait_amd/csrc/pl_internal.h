@@ -27,7 +27,12 @@ struct AttnLaunch {
   int32_t nseg;
   AttnSegment seg[PL_MAX_SEGMENTS];
   float scale;
+  void* workspace;  // >= refbank_attn_workspace_bytes(...) bytes, 16-byte aligned, or nullptr (no key split)
 };
+
+// Bytes of workspace the launch below uses for these sizes (0: it splits nothing).
+size_t refbank_attn_workspace_bytes(int32_t F, int32_t Lq, int32_t H, int32_t d, const int64_t* seg_len,
+                                    int32_t nseg);
 
 // Launch the flash-style MFMA attention for one layer on `stream`.
 hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream);

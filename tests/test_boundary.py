@@ -128,9 +128,47 @@ def test_attention_fused_column_slices(lib):
     assert st == B.PL_EINVAL and "segment 0" in B.last_error()
 
 
-def test_workspace_size_is_zero(lib):
-    lens = (ctypes.c_int64 * 2)(4096, 4096)
-    assert lib.pl_refbank_attn_workspace_size(16, 4096, 8, 40, lens, 2) == 0
+def _wsize(lib, F, L, H, d, lens):
+    arr = (ctypes.c_int64 * max(1, len(lens)))(*lens)
+    return lib.pl_refbank_attn_workspace_size(F, L, H, d, arr, len(lens))
+
+
+def test_workspace_size(lib):
+    # launches that fill the CUs, or whose key axis is too short to split, need none
+    assert _wsize(lib, 16, 4096, 8, 40, [4096] * 5) == 0
+    assert _wsize(lib, 16, 1024, 8, 80, [1024] * 5) == 0
+    assert _wsize(lib, 16, 256, 8, 160, [256] * 5) == 0
+    assert _wsize(lib, 16, 64, 8, 160, [64] * 5) == 0
+    # one frame of the 16^2 level with the 4x bank (20 key tiles, 16 workgroups):
+    # two splits of ten tiles; partial O, offset and row sum in fp32 per
+    # (frame, head, split, row)
+    assert _wsize(lib, 1, 256, 8, 160, [256] * 5) == 1 * 8 * 2 * 256 * (160 + 2) * 4
+    # 41 tiles, one workgroup: five splits of at least eight tiles
+    assert _wsize(lib, 1, 40, 1, 160, [64, 1024, 1024, 512]) == 5 * 40 * 162 * 4
+    # a single key tile has nothing to split; short contexts take their own kernel
+    assert _wsize(lib, 1, 64, 8, 160, [64]) == 0
+    assert _wsize(lib, 1, 64, 8, 160, [32]) == 0
+    # invalid sizes report 0 (the call itself rejects them)
+    assert _wsize(lib, 1, 256, 8, 48, [256] * 5) == 0
+    assert _wsize(lib, 0, 256, 8, 160, [256] * 5) == 0
+    assert lib.pl_refbank_attn_workspace_size(1, 256, 8, 160, None, 5) == 0
+
+
+def test_attention_rejects_small_workspace(lib):
+    # a one-frame 16^2 launch splits its keys and needs a workspace: too small
+    # or NULL with bytes is rejected before any launch; misaligned is unsupported
+    F, L, C, H = 1, 256, 1280, 8
+    n = _wsize(lib, F, L, H, 160, [256] * 5)
+    assert n > 0
+    segs = _segs((ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000), 256, C, L * C),
+                 *[(ctypes.c_void_p(0x3000000 + 0x100000 * i), ctypes.c_void_p(0x4000000 + 0x100000 * i), 256, C, 0)
+                   for i in range(4)])
+    def call(ws, nbytes):
+        return B.pl_refbank_attn(ctypes.c_void_p(0x5000000), C, L * C, ctypes.c_void_p(0x6000000), C, L * C, F, L, H,
+                                 160, segs, 5, 0.08, ws, nbytes, None)
+    assert call(ctypes.c_void_p(0x9000000), n - 16) == B.PL_EINVAL and "too small" in B.last_error()
+    assert call(None, n) == B.PL_EINVAL and "NULL" in B.last_error()
+    assert call(ctypes.c_void_p(0x9000008), n) == B.PL_EUNSUPPORTED and "workspace" in B.last_error()
 
 
 def _ddim(x=A, e=A, xp=A2, x0=A, W=4, n=256, t=(999, 666, 333, 0), step=333, ab=None, T=1000, fin=-1.0, emit=3):
