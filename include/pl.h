@@ -113,6 +113,24 @@ pl_status pl_refbank_attn(const void* q, int64_t q_ld, int64_t q_frame_stride,
                           const pl_kv_segment* segs, int32_t nseg, float scale,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* pl_refbank_attn without a caller workspace, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, layout, results and
+ * errors as pl_refbank_attn, without workspace / workspace_bytes: the launches
+ * that split the key axis put their partials in a scratch array the library
+ * holds on each GPU (16 MiB, kept until the process ends; its address is
+ * looked up once per device, with that device current, on the first call
+ * there).  Nothing is allocated, freed or cleared by a call.
+ * PL_EINVAL if the split of these sizes needs more than 16 MiB of scratch
+ * (pl_refbank_attn_workspace_size reports what it needs); PL_EDEVICE if the
+ * scratch's address cannot be obtained.  Every call on one GPU shares that
+ * scratch and leaves its own partials there: calls that overlap in time on
+ * one GPU (concurrent streams, or threads) race and must not be issued. */
+pl_status pl_refbank_attn_noalloc(const void* q, int64_t q_ld, int64_t q_frame_stride,
+                                  void* o, int64_t o_ld, int64_t o_frame_stride,
+                                  int32_t F, int32_t Lq, int32_t H, int32_t d,
+                                  const pl_kv_segment* segs, int32_t nseg, float scale, void* stream);
+
 /* ------------------------------------------------------------------------ *
  * Projections either side of the attention
  *

@@ -30,6 +30,7 @@ EXPORTED = (
     "pl_last_error",
     "pl_refbank_attn_workspace_size",
     "pl_refbank_attn",
+    "pl_refbank_attn_noalloc",
     "pl_pyramid_ddim_step",
     "pl_pyramid_ddim_step_roll",
     "pl_sd_alphas_cumprod",
@@ -102,6 +103,9 @@ def load():
     lib.pl_refbank_attn.restype = i32
     lib.pl_refbank_attn.argtypes = [vp, i64, i64, vp, i64, i64, i32, i32, i32, i32,
                                     ctypes.POINTER(pl_kv_segment), i32, f32, vp, sz, vp]
+    lib.pl_refbank_attn_noalloc.restype = i32
+    lib.pl_refbank_attn_noalloc.argtypes = [vp, i64, i64, vp, i64, i64, i32, i32, i32, i32,
+                                            ctypes.POINTER(pl_kv_segment), i32, f32, vp]
     lib.pl_pyramid_ddim_step.restype = i32
     lib.pl_pyramid_ddim_step.argtypes = [vp, vp, vp, vp, i32, i64, ctypes.POINTER(i32), i32,
                                          ctypes.POINTER(f64), i32, f64, i32, vp]
@@ -150,6 +154,10 @@ def _check(name, status):
 # ---- raw entry points, same names as the C ABI ----------------------------------
 def pl_refbank_attn(*args):
     return load().pl_refbank_attn(*args)
+
+
+def pl_refbank_attn_noalloc(*args):
+    return load().pl_refbank_attn_noalloc(*args)
 
 
 def pl_refbank_attn_workspace_size(*args):

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "pl_internal.h"
 
@@ -176,10 +177,46 @@ size_t pl_refbank_attn_workspace_size(int32_t F, int32_t Lq, int32_t H, int32_t 
   return pl::refbank_attn_workspace_bytes(F, Lq, H, d, seg_len, nseg);
 }
 
-pl_status pl_refbank_attn(const void* q, int64_t q_ld, int64_t q_frame_stride, void* o, int64_t o_ld,
-                          int64_t o_frame_stride, int32_t F, int32_t Lq, int32_t H, int32_t d,
-                          const pl_kv_segment* segs, int32_t nseg, float scale, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Scratch of the allocation-free attention call: the key-split partials go to
+// this device array instead of a caller workspace.  Each GPU holds its own
+// copy for the life of the process.  Host code never uses the array's name
+// as an address (on the host it is a stand-in): the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+pl_status scratch_for_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PL_EDEVICE, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PL_EUNSUPPORTED, "%s: device index %d beyond %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(PL_EDEVICE, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    if (!ptr) return fail(PL_EDEVICE, "%s: hipGetSymbolAddress(scratch) returned NULL", fn);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PL_OK;
+}
+
+// pl_refbank_attn and its allocation-free variant (noalloc: the key-split
+// partials go to the library's scratch; workspace arguments are unused).
+pl_status refbank_attn_impl(const char* fn, const void* q, int64_t q_ld, int64_t q_frame_stride, void* o,
+                            int64_t o_ld, int64_t o_frame_stride, int32_t F, int32_t Lq, int32_t H, int32_t d,
+                            const pl_kv_segment* segs, int32_t nseg, float scale, void* workspace,
+                            size_t workspace_bytes, bool noalloc, void* stream) {
+  (void)fn;
   if (!q || !o) return fail(PL_EINVAL, "pl_refbank_attn: q and o must be non-null");
   if (!segs) return fail(PL_EINVAL, "pl_refbank_attn: segs must be non-null");
   if (F < 1 || Lq < 1 || H < 1) return fail(PL_EINVAL, "pl_refbank_attn: F, Lq, H must be >= 1 (got %d, %d, %d)", F, Lq, H);
@@ -234,7 +271,14 @@ pl_status pl_refbank_attn(const void* q, int64_t q_ld, int64_t q_frame_stride, v
   for (int i = 0; i < nseg; ++i) lens[i] = segs[i].len;
   const size_t need = pl::refbank_attn_workspace_bytes(F, Lq, H, d, lens, nseg);
   a.workspace = nullptr;
-  if (workspace || workspace_bytes) {
+  if (noalloc) {
+    if (need > kScratchBytes)
+      return fail(PL_EINVAL, "%s: the key split of these sizes needs %zu bytes of scratch; the library holds %zu", fn,
+                  need, kScratchBytes);
+    if (need > 0) {
+      if (pl_status st = scratch_for_current_device(fn, &a.workspace)) return st;
+    }
+  } else if (workspace || workspace_bytes) {
     if (!workspace) return fail(PL_EINVAL, "pl_refbank_attn: workspace_bytes is %zu but workspace is NULL", workspace_bytes);
     if (workspace_bytes < need)
       return fail(PL_EINVAL, "pl_refbank_attn: workspace of %zu bytes is too small (%zu needed)", workspace_bytes, need);
@@ -254,6 +298,25 @@ pl_status pl_refbank_attn(const void* q, int64_t q_ld, int64_t q_frame_stride, v
   a.nseg = nseg;
   a.scale = scale;
   return device_status(pl::launch_refbank_attn(a, static_cast<hipStream_t>(stream)), "pl_refbank_attn launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+pl_status pl_refbank_attn(const void* q, int64_t q_ld, int64_t q_frame_stride, void* o, int64_t o_ld,
+                          int64_t o_frame_stride, int32_t F, int32_t Lq, int32_t H, int32_t d,
+                          const pl_kv_segment* segs, int32_t nseg, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return refbank_attn_impl("pl_refbank_attn", q, q_ld, q_frame_stride, o, o_ld, o_frame_stride, F, Lq, H, d, segs,
+                           nseg, scale, workspace, workspace_bytes, false, stream);
+}
+
+pl_status pl_refbank_attn_noalloc(const void* q, int64_t q_ld, int64_t q_frame_stride, void* o, int64_t o_ld,
+                                  int64_t o_frame_stride, int32_t F, int32_t Lq, int32_t H, int32_t d,
+                                  const pl_kv_segment* segs, int32_t nseg, float scale, void* stream) {
+  return refbank_attn_impl("pl_refbank_attn_noalloc", q, q_ld, q_frame_stride, o, o_ld, o_frame_stride, F, Lq, H, d,
+                           segs, nseg, scale, nullptr, 0, true, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -326,3 +326,20 @@ def test_ddim_device_rejects(lib, kw, status):
                                        a["fin"], 7, None)
     assert st == status
     assert B.last_error() != ""
+
+
+def test_noalloc_rejects_split_beyond_its_scratch(lib):
+    # one frame of a 2048-row d = 160 level with a 4x bank: two splits of
+    # 2048 rows x 8 heads need about 21 MB of partials, more than the 16 MiB
+    # the library holds; rejected before any device call
+    F, L, C, H = 1, 2048, 1280, 8
+    assert _wsize(lib, F, L, H, 160, [L] * 5) > 16 << 20
+    segs = _segs((ctypes.c_void_p(0x10000000), ctypes.c_void_p(0x20000000), L, C, L * C),
+                 *[(ctypes.c_void_p(0x30000000 + 0x1000000 * i), ctypes.c_void_p(0x40000000 + 0x1000000 * i), L, C, 0)
+                   for i in range(4)])
+    st = B.pl_refbank_attn_noalloc(ctypes.c_void_p(0x50000000), C, L * C, ctypes.c_void_p(0x60000000), C, L * C, F,
+                                   L, H, 160, segs, 5, 0.08, None)
+    assert st == B.PL_EINVAL and "scratch" in B.last_error()
+    # argument checks are those of pl_refbank_attn
+    assert B.pl_refbank_attn_noalloc(None, C, L * C, ctypes.c_void_p(0x60000000), C, L * C, F, L, H, 160, segs, 5,
+                                     0.08, None) == B.PL_EINVAL
