@@ -366,6 +366,28 @@ def main():
         del sq, sk, sv, so, scall
     log("  expression cross-attention (32 keys/frame): " +
         ", ".join(f"L={r['L']} {r['us']:.1f} us {r['GBps']:.0f} GB/s" for r in short_ctx))
+    # the key-axis split: one frame of the 16^2 and 8^2 levels against the 4x bank (the
+    # round's own launches fill the CUs and do not split), split and single pass
+    key_split = []
+    for L in (256, 64):
+        g = torch.Generator(device=dev).manual_seed(11 * L)
+        kq = torch.randn(1, L, 1280, device=dev, generator=g).half()
+        ksegs = [(torch.randn(1, L, 1280, device=dev, generator=g).half(),
+                  torch.randn(1, L, 1280, device=dev, generator=g).half())]
+        ksegs += [(torch.randn(L, 1280, device=dev, generator=g).half(),
+                   torch.randn(L, 1280, device=dev, generator=g).half()) for _ in range(4)]
+        ko = torch.empty_like(kq)
+        rec = dict(L=L, C=1280, frames=1, keys=5 * L)
+        for mode, ws in (("split", None), ("single_pass", False)):
+            kcall = B.PreparedAttn(kq, ksegs, H, ko, workspace=ws)
+            rec[f"{mode}_us"] = round(time_it(kcall, n=100), 2)
+            if mode == "split":
+                rec["workspace_bytes"] = kcall.workspace_bytes
+            del kcall
+        key_split.append(rec)
+        del kq, ksegs, ko
+    log("  key split (one frame, 4x bank): " +
+        ", ".join(f"L={r['L']} split {r['split_us']:.1f} us / single {r['single_pass_us']:.1f} us" for r in key_split))
     # the projections either side of the attention: fused q/k/v ([3C, C]) and the
     # output projection ([C, C] + bias) over the 16 frames of each level
     projections = []
@@ -484,6 +506,7 @@ def main():
                  "us_with_roll_at_round_shape": round(roll_us, 2), "sweep": sweep},
         "pile_prefill_us": round(prefill_us, 2),
         "expression_cross_attention": short_ctx,
+        "key_split_one_frame": key_split,
         "projections": projections,
         "motion_us": round(motion_us, 2),
         "layers": layer_report,

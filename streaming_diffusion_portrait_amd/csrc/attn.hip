@@ -98,18 +98,13 @@ constexpr int kSchedMfma = 0x008, kSchedValu = 0x002, kSchedDsRead = 0x100;
 // for e >= 4, with vrow(g) = 0, 8, 4, 12 for g = 0..3.
 __device__ __forceinline__ int vrow(int g) { return 8 * (g & 1) + 4 * (g >> 1); }
 
-// d = 40 layers: O^T += V^T P^T on 32x32x16 products (1) or 16x16x32 ones (0).
-#ifndef PL_D40_PV32
-#define PL_D40_PV32 0
-#endif
-
 // Bytes of padding after each 1 KB plane of a staged tile; it moves the two
 // planes one transposing read touches onto different LDS banks.
 #ifndef PL_PLANE_PAD
 #define PL_PLANE_PAD 64
 #endif
 
-template <int D_, int NQB_, int NKB_, int NBUF_, int MINB_, bool PIPE_, int W_, bool PV32_ = false>
+template <int D_, int NQB_, int NKB_, int NBUF_, int MINB_, bool PIPE_, int W_>
 struct Cfg {
   static constexpr int D = D_;
   static constexpr int W = W_;                // wavefronts per workgroup
@@ -122,13 +117,7 @@ struct Cfg {
   static constexpr int BN = 32 * NKB;         // keys per tile
   static constexpr int QWG = 32 * NQB * W;     // query rows per workgroup
   static constexpr int KST = (D + 15) / 16;   // 16-wide contraction steps of S^T
-  static constexpr int NDT = (D + 15) / 16;   // 16-row tiles of O^T (16x16x32 PV products)
-  // PV32: O^T += V^T P^T on v_mfma_f32_32x32x16_f16 instead (32-row tiles,
-  // 16 keys per product): P^T then comes straight from the S^T accumulator
-  // layout (no lane swaps) and the row sums from the ones row of V^T's padding
-  static constexpr bool PV32 = PV32_;
-  static constexpr int NRT = (D + 1 + 31) / 32;  // 32-row O^T tiles (the ones row included)
-  static constexpr int NVA = PV32 ? 2 * NRT : NDT;  // V^T operands per 32-key block
+  static constexpr int NDT = (D + 15) / 16;   // 16-row tiles of O^T
   static constexpr bool ONES = (D % 16) != 0; // padding column D carries ones / -m
   // no ones column (d = 32, 80, 160): the row sums come from two more PV
   // products per query block with a constant A whose first row is ones (with
@@ -150,8 +139,6 @@ struct Cfg {
   static_assert(PLB % 16 == 0, "planes hold 16-byte chunks");
   static_assert(NBUF >= 2 && NBUF <= 6, "ring of 2 to 6 buffers");
   static_assert(NI * (NBUF - 1) <= 48, "vmcnt wait table range");
-  static_assert(!PV32 || ONES, "32-row PV tiles take the row sums from the ones row at dim D of the padding");
-  static_assert(!PV32 || NRT <= 3, "lane offsets for up to three 32-row O^T tiles");
 };
 
 struct KParams {
@@ -341,7 +328,6 @@ template <class C>
 struct WaveState {
   h8 qf[C::NQB][C::KST];       // Q^T operands (scaled, fp16)
   f4 oacc[C::NQB][2][C::NDT];  // O^T accumulators: [query block][16-query half][16-row d tile]
-  f16v oacc32[C::NQB][C::NRT];  // PV32: O^T accumulators [query block][32-row d tile]
   float mrun[C::NQB];          // running offset of query l%32 of each block
   f16v negm[C::NQB];           // -mrun in every accumulator slot: the seed of fast S^T products (no ones column)
   f4 osum[C::NQB][2];          // RSUM: row 0 holds the row sums of the half's 16 queries
@@ -353,7 +339,6 @@ struct LaneCtx {
   int lane, h, c16, g;
   int krow_off;     // K operand LDS byte offset within a 32-key block (plane 0)
   int vrow_off[2];  // V^T operand LDS byte offsets of the two transposing reads (planes 0, 1)
-  int v32_off[3][2];  // PV32: byte offsets of the transposing reads [32-row tile][key run] (key step 0)
 };
 
 // K operands of one 32-key block: step st reads planes 2st (lanes 0..31)
@@ -392,26 +377,7 @@ __device__ __forceinline__ void qk_block(const char* smem, int kblk, const WaveS
 
 // V^T operands of one 32-key block.
 template <class C>
-__device__ __forceinline__ void load_vt(const char* smem, int vblk, const LaneCtx& lc, h8 (&va)[C::NVA]) {
-  if constexpr (C::PV32) {
-    // operand (t, s): rows 32t.. of V^T, keys 16s.. of the block; lane (g, c16)
-    // gets dim 32t + 16(g%2) + c16 of keys 16s + 4(g/2) + 0..3 (read 0) and
-    // 16s + 8 + 4(g/2) + 0..3 (read 1)
-#pragma unroll
-    for (int t = 0; t < C::NRT; ++t)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(smem + vblk + 256 * st + lc.v32_off[t][0]));
-        const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(smem + vblk + 256 * st + lc.v32_off[t][1]));
-        u4 w;
-        w[0] = __builtin_bit_cast(unsigned, (s2){lo[0], lo[1]});
-        w[1] = __builtin_bit_cast(unsigned, (s2){lo[2], lo[3]});
-        w[2] = __builtin_bit_cast(unsigned, (s2){hi[0], hi[1]});
-        w[3] = __builtin_bit_cast(unsigned, (s2){hi[2], hi[3]});
-        va[2 * t + st] = __builtin_bit_cast(h8, w);
-      }
-    return;
-  }
+__device__ __forceinline__ void load_vt(const char* smem, int vblk, const LaneCtx& lc, h8 (&va)[C::NDT]) {
 #pragma unroll
   for (int t = 0; t < C::NDT; ++t) {
     const int a0 = vblk + 2 * t * C::PLB + lc.vrow_off[0];
@@ -429,17 +395,7 @@ __device__ __forceinline__ void load_vt(const char* smem, int vblk, const LaneCt
 
 // O^T += V^T P^T for one 32-key block.
 template <class C>
-__device__ __forceinline__ void pv_block(const h8 (&va)[C::NVA], const h8 (&pb)[C::NQB][2], WaveState<C>& ws) {
-  if constexpr (C::PV32) {
-#pragma unroll
-    for (int t = 0; t < C::NRT; ++t)
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb)
-          ws.oacc32[qb][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[2 * t + st], pb[qb][st], ws.oacc32[qb][t], 0, 0, 0);
-    return;
-  }
+__device__ __forceinline__ void pv_block(const h8 (&va)[C::NDT], const h8 (&pb)[C::NQB][2], WaveState<C>& ws) {
 #pragma unroll
   for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
@@ -518,28 +474,15 @@ __device__ __forceinline__ void softmax_block(f16v (&sacc)[C::NQB], WaveState<C>
       for (int x = 0; x < 2; ++x)
         pk[i][x] = pack_h2(__builtin_amdgcn_exp2f(sacc[qb][4 * i + 2 * x]),
                            __builtin_amdgcn_exp2f(sacc[qb][4 * i + 2 * x + 1]));
-    u4 b0, b1;
-    if constexpr (C::PV32) {
-      // P^T for keys 0..15 and 16..31 of the block, in the lane's own S^T
-      // order: contraction index 8h + e is key 16s + 4h + e (e < 4) or
-      // 16s + 8 + 4h + e - 4 (e >= 4)
+    u4 b0, b1;  // P^T for queries 0..15 and 16..31 of the block
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        b0[x] = pk[0][x];
-        b0[2 + x] = pk[1][x];
-        b1[x] = pk[2][x];
-        b1[2 + x] = pk[3][x];
-      }
-    } else {  // P^T for queries 0..15 and 16..31 of the block
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const auto s01 = __builtin_amdgcn_permlane16_swap(pk[0][x], pk[1][x], false, false);
-        const auto s23 = __builtin_amdgcn_permlane16_swap(pk[2][x], pk[3][x], false, false);
-        b0[x] = s01[0];
-        b1[x] = s01[1];
-        b0[2 + x] = s23[0];
-        b1[2 + x] = s23[1];
-      }
+    for (int x = 0; x < 2; ++x) {
+      const auto s01 = __builtin_amdgcn_permlane16_swap(pk[0][x], pk[1][x], false, false);
+      const auto s23 = __builtin_amdgcn_permlane16_swap(pk[2][x], pk[3][x], false, false);
+      b0[x] = s01[0];
+      b1[x] = s01[1];
+      b0[2 + x] = s23[0];
+      b1[2 + x] = s23[1];
     }
     pb[qb][0] = __builtin_bit_cast(h8, b0);
     pb[qb][1] = __builtin_bit_cast(h8, b1);
@@ -549,13 +492,6 @@ __device__ __forceinline__ void softmax_block(f16v (&sacc)[C::NQB], WaveState<C>
 // O^T *= alpha (alpha given in S layout, moved to the O^T layout).
 template <class C>
 __device__ __forceinline__ void rescale_acc(WaveState<C>& ws, const LaneCtx& lc, const float (&alpha)[C::NQB]) {
-  if constexpr (C::PV32) {  // the O^T columns of a lane are its own S^T query
-#pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb)
-#pragma unroll
-      for (int t = 0; t < C::NRT; ++t) ws.oacc32[qb][t] *= alpha[qb];
-    return;
-  }
 #pragma unroll
   for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
@@ -576,7 +512,7 @@ __device__ __forceinline__ void tile_step(const char* smem, int kt, int valid, b
     if (kb > 0 && valid <= 32 * kb) break;  // a tile's last block holds no key (short segments)
     f16v s[C::NQB];
     qk_block<C, FAST && !C::ONES>(smem, kt + kb * C::KBLK, ws, lc, s);
-    h8 va[C::NVA];
+    h8 va[C::NDT];
     load_vt<C>(smem, kt + C::TILEB + kb * C::KBLK, lc, va);
     h8 pb[C::NQB][2];
     float alpha[C::NQB];
@@ -598,7 +534,7 @@ __device__ __forceinline__ void sched_iteration() {
   // registers) threaded with the softmax's vector work; then the reads of the
   // next K operands (into the registers those products just read) and the PV
   // products with the rest of the vector work
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * C::NVA, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * C::NDT, 0);
 #pragma unroll
   for (int i = 0; i < C::NQB * C::KST; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
@@ -606,7 +542,7 @@ __device__ __forceinline__ void sched_iteration() {
   }
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::KST, 0);
 #pragma unroll
-  for (int i = 0; i < C::NQB * (C::PV32 ? 2 * C::NRT : 2 * C::NDT); ++i) {
+  for (int i = 0; i < C::NQB * 2 * C::NDT; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedValu, PL_SCHED_PER, 0);
   }
@@ -620,7 +556,7 @@ __device__ __forceinline__ void sched_iteration() {
 // block.
 template <class C>
 constexpr int sm_ops() {
-  return C::PV32 ? 24 : 28;  // 16 exponentials, 8 packs (+ 4 swaps for the 16x16 PV layout)
+  return 28;
 }
 template <class C>
 struct FastSoftmax {
@@ -639,16 +575,7 @@ struct FastSoftmax {
     } else if (r < 24) {  // packs 6, 7
       const int i = r - 16;
       pk[qb][i] = pack_h2(s[qb][2 * i], s[qb][2 * i + 1]);
-    }
-    if constexpr (C::PV32) {
-      // pack i (keys of run i/2, pair i%2) is dword i%4 of P^T operand i/4
-      if (r >= 4 && r < 24 && (r >= 22 || (r - 4) % 3 == 0)) {
-        const int i = r < 22 ? (r - 4) / 3 : r - 16;
-        u4 b = __builtin_bit_cast(u4, pb[2 * qb + i / 4]);
-        b[i % 4] = pk[qb][i];
-        pb[2 * qb + i / 4] = __builtin_bit_cast(h8, b);
-      }
-    } else if (r >= 24) {  // swaps: pack (2j+x) with pack (2j+2+x) for j = 0, 2 and x = 0, 1
+    } else {  // swaps: pack (2j+x) with pack (2j+2+x) for j = 0, 2 and x = 0, 1
       const int k = r - 24, x = k & 1, j = (k >> 1) * 4;
       const auto sw = __builtin_amdgcn_permlane16_swap(pk[qb][j + x], pk[qb][j + 2 + x], false, false);
       u4 b0 = __builtin_bit_cast(u4, pb[2 * qb]), b1 = __builtin_bit_cast(u4, pb[2 * qb + 1]);
@@ -671,16 +598,6 @@ struct FastSoftmax {
 #ifndef PL_SLOT_PV
 #define PL_SLOT_PV 3
 #endif
-#ifndef PL_SLOT32_QK
-#define PL_SLOT32_QK 4
-#endif
-#ifndef PL_SLOT32_PV
-#define PL_SLOT32_PV 3
-#endif
-#ifndef PL_PV32_PRIO
-#define PL_PV32_PRIO 1
-#endif
-
 // Steady pipelined iteration with a fixed instruction order: the LDS reads,
 // then slots of one matrix product and a share of the softmax's vector
 // instructions, fenced so that the compiler keeps the interleave.  Computes
@@ -690,15 +607,13 @@ __device__ __forceinline__ void pipe_iteration_fixed(const char* smem, int vblk,
                                                      f16v (&s_out)[C::NQB], const h8 (&p_in)[C::NQB][2],
                                                      h8 (&p_out)[C::NQB][2], const h8 (&ka_cur)[C::KST],
                                                      h8 (&ka_next)[C::KST], WaveState<C>& ws, const LaneCtx& lc) {
-  constexpr int NQK = C::KST * C::NQB;
-  constexpr int NPV = C::PV32 ? 2 * C::NRT * C::NQB : (C::NDT + (C::RSUM ? 1 : 0)) * C::NQB * 2;
-  constexpr int NM = NQK + NPV;
+  constexpr int NQK = C::KST * C::NQB, NPV = (C::NDT + (C::RSUM ? 1 : 0)) * C::NQB * 2, NM = NQK + NPV;
   constexpr int NV = sm_ops<C>() * C::NQB;
   // vector instructions after each S^T / PV product (d = 40: tuned; otherwise
   // 4 after each S^T product and the rest spread over the PV products)
-  constexpr int SQK = C::PV32 ? PL_SLOT32_QK : C::ONES ? PL_SLOT_QK : 4;
-  constexpr int SPV = C::PV32 ? PL_SLOT32_PV : C::ONES ? PL_SLOT_PV : (NV - NQK * SQK + NPV - 1) / NPV;
-  h8 va[C::NVA];
+  constexpr int SQK = C::ONES ? PL_SLOT_QK : 4;
+  constexpr int SPV = C::ONES ? PL_SLOT_PV : (NV - NQK * SQK + NPV - 1) / NPV;
+  h8 va[C::NDT];
   load_vt<C>(smem, vblk, lc, va);
   load_k<C>(smem, kblk3, lc, ka_next);
   __builtin_amdgcn_sched_barrier(0);
@@ -718,9 +633,6 @@ __device__ __forceinline__ void pipe_iteration_fixed(const char* smem, int vblk,
       const int st = m / C::NQB, qb = m % C::NQB;
       s_out[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
           ka_cur[st], ws.qf[qb][st], st > 0 ? s_out[qb] : C::ONES ? (f16v){} : ws.negm[qb], 0, 0, 0);
-    } else if constexpr (C::PV32) {  // O^T += V^T(b) P^T(b): d tiles, then key steps, outermost
-      const int i = m - NQK, t = i / (2 * C::NQB), st = (i / C::NQB) % 2, qb = i % C::NQB;
-      ws.oacc32[qb][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[2 * t + st], p_in[qb][st], ws.oacc32[qb][t], 0, 0, 0);
     } else {  // O^T += V^T(b) P^T(b): d tiles outermost (the V reads land in that order), then the row sums
       const int i = m - NQK, t = i / (2 * C::NQB), qb = (i / 2) % C::NQB, grp = i % 2;
       if (t < C::NDT)
@@ -741,88 +653,6 @@ __device__ __forceinline__ void pipe_iteration_fixed(const char* smem, int vblk,
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Steady pipelined iteration for 32-row PV tiles (two query blocks per wave),
-// in an order that keeps the register peak low: the PV(b) products first
-// (V^T(b) read during the previous iteration), then the S^T(b+2) products;
-// V^T(b+1) is read after the last PV product and K(b+3) after the last S^T
-// product, so each operand set is dead before its successor lands.  The
-// softmax of block b+1 runs under both: query block 0's exponentials, then
-// query block 1's with block 0's packs between them, then block 1's packs --
-// so P(b+1) is mostly built after P(b) has been consumed.
-template <class C>
-__device__ __forceinline__ void pipe_iteration_pv32(const char* smem, int vblk_next, int kblk3, f16v (&s_in)[C::NQB],
-                                                    f16v (&s_out)[C::NQB], const h8 (&p_in)[C::NQB][2],
-                                                    h8 (&p_out)[C::NQB][2], const h8 (&ka_cur)[C::KST],
-                                                    h8 (&ka_next)[C::KST], const h8 (&va_cur)[C::NVA],
-                                                    h8 (&va_next)[C::NVA], WaveState<C>& ws, const LaneCtx& lc) {
-  static_assert(C::PV32 && C::NQB == 2, "written for two query blocks and 32-row PV tiles");
-  constexpr int NPV = 2 * C::NRT * C::NQB, NQK = C::KST * C::NQB, NM = NPV + NQK, NV = 48;
-  unsigned pk[2][8];
-  auto op = [&](int v) {
-    if (v < 16) {  // query block 0: exponentials
-      s_in[0][v] = __builtin_amdgcn_exp2f(s_in[0][v]);
-    } else if (v < 40) {  // query block 1: two exponentials, then one pack of block 0
-      const int g = (v - 16) / 3, k = (v - 16) % 3;
-      if (k < 2) {
-        s_in[1][2 * g + k] = __builtin_amdgcn_exp2f(s_in[1][2 * g + k]);
-      } else {
-        pk[0][g] = pack_h2(s_in[0][2 * g], s_in[0][2 * g + 1]);
-        u4 b = __builtin_bit_cast(u4, p_out[0][g / 4]);
-        b[g % 4] = pk[0][g];
-        p_out[0][g / 4] = __builtin_bit_cast(h8, b);
-      }
-    } else {  // query block 1: packs
-      const int i = v - 40;
-      pk[1][i] = pack_h2(s_in[1][2 * i], s_in[1][2 * i + 1]);
-      u4 b = __builtin_bit_cast(u4, p_out[1][i / 4]);
-      b[i % 4] = pk[1][i];
-      p_out[1][i / 4] = __builtin_bit_cast(h8, b);
-    }
-  };
-  int v = 0;
-#if PL_PV32_PRIO
-  __builtin_amdgcn_s_setprio(1);
-#endif
-#pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    if (m < NPV) {  // O^T += V^T(b) P^T(b): d tiles, then key steps, outermost
-      const int t = m / (2 * C::NQB), st = (m / C::NQB) % 2, qb = m % C::NQB;
-      ws.oacc32[qb][t] =
-          __builtin_amdgcn_mfma_f32_32x32x16_f16(va_cur[2 * t + st], p_in[qb][st], ws.oacc32[qb][t], 0, 0, 0);
-    } else {  // S^T(b+2): steps outermost, query blocks alternate
-      const int st = (m - NPV) / C::NQB, qb = (m - NPV) % C::NQB;
-      s_out[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka_cur[st], ws.qf[qb][st], st > 0 ? s_out[qb] : (f16v){},
-                                                         0, 0, 0);
-    }
-    const int nv = m < NPV ? PL_SLOT32_PV : PL_SLOT32_QK;
-#pragma unroll
-    for (int k = 0; k < nv; ++k)
-      if (v + k < NV) op(v + k);
-    v += nv;
-    if (m == NPV - 1) {
-#if PL_PV32_PRIO
-      __builtin_amdgcn_s_setprio(0);
-#endif
-      load_vt<C>(smem, vblk_next, lc, va_next);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int k = 0; k < NV; ++k)
-    if (k >= v) op(k);
-  load_k<C>(smem, kblk3, lc, ka_next);
-  // The products and the softmax have no side effects and their results are
-  // only read by the next iteration, past a barrier and branches: without
-  // these (empty) uses the compiler sinks them there and the interleave above
-  // is lost.
-#pragma unroll
-  for (int qb = 0; qb < C::NQB; ++qb) {
-    asm volatile("" : "+v"(p_out[qb][0]), "+v"(p_out[qb][1]));
-    asm volatile("" : "+v"(s_out[qb]));
-  }
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // One pipelined iteration over full blocks (block b of the pipeline):
 //   S^T(b+2) = K(b+2) Q^T from K operands already in registers (ka_cur),
 //   K operands of block b+3 read from LDS into ka_next,
@@ -838,7 +668,7 @@ __device__ __forceinline__ void pipe_iteration(const char* smem, int vblk, int k
                                                h8 (&ka_next)[C::KST], WaveState<C>& ws, const LaneCtx& lc) {
   float alpha[C::NQB];
   bool resc;
-  h8 va[C::NVA];
+  h8 va[C::NDT];
   load_vt<C>(smem, vblk, lc, va);
   if (QK) qk_regs<C, !C::ONES>(ka_cur, ws, s_out);  // pipelined blocks are fast
   if (SM) softmax_block<C, false>(s_in, ws, lc, 32, false, p_out, alpha, resc);
@@ -931,19 +761,6 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
 #pragma unroll
   for (int r = 0; r < 2; ++r)
     lc.vrow_off[r] = (vrow(lc.g) + 16 * r + (lc.c16 >> 2)) * 16 + ((lc.c16 & 3) >> 1) * C::PLB + 8 * (lc.c16 & 1);
-  if constexpr (C::PV32) {
-    // 32-row tile t, read r: key 8r + 4(g/2) + c16/4 of the 16-key step, dims
-    // 32t + 16(g%2) + 4(c16%4) .. +3; rows past the last plane (their O^T rows
-    // are never used) re-read the two planes before them
-#pragma unroll
-    for (int t = 0; t < C::NRT; ++t)
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        int plane = (32 * t + 16 * (lc.g & 1) + 4 * (lc.c16 & 3)) / 8;
-        while (plane >= C::NPL) plane -= 2;
-        lc.v32_off[t][r] = (8 * r + 4 * (lc.g >> 1) + (lc.c16 >> 2)) * 16 + plane * C::PLB + 8 * (lc.c16 & 1);
-      }
-  }
 
   // Tiles in the key sequence (this split's range of them) and this wave's
   // copy instructions per tile.
@@ -995,8 +812,6 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
       for (int grp = 0; grp < 2; ++grp)
 #pragma unroll
         for (int t = 0; t < C::NDT; ++t) ws.oacc[qb][grp][t] = (f4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < C::NRT; ++t) ws.oacc32[qb][t] = (f16v){};
       if constexpr (C::RSUM) ws.osum[qb][0] = ws.osum[qb][1] = (f4){0.f, 0.f, 0.f, 0.f};
       if constexpr (C::ONES) if (lc.h) ws.qf[qb][C::KST - 1][0] = (_Float16)0.0f;  // offset column: none yet
     }
@@ -1063,7 +878,6 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
       f16v sA[C::NQB], sB[C::NQB];
       h8 pA[C::NQB][2], pB[C::NQB][2];
       h8 kaA[C::KST], kaB[C::KST];
-      h8 vaA[C::NVA], vaB[C::NVA];  // PV32: V^T(b) is read one iteration ahead
       {
         float alpha[C::NQB];
         bool resc;
@@ -1071,18 +885,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
         softmax_block<C, false>(sA, ws, lc, 32, false, pA, alpha, resc);
         qk_block<C, !C::ONES>(smem, kblk(1), ws, lc, sB);
         if (2 < nb) load_k<C>(smem, kblk(2), lc, kaA);
-        if constexpr (C::PV32) load_vt<C>(smem, vblk(0), lc, vaA);
       }
-      // a steady iteration of block j (even j: the A sets feed it; odd j: the B sets)
-      auto steady = [&](int j, f16v(&s_in)[C::NQB], f16v(&s_out)[C::NQB], const h8(&p_in)[C::NQB][2],
-                        h8(&p_out)[C::NQB][2], const h8(&ka_cur)[C::KST], h8(&ka_next)[C::KST],
-                        const h8(&va_cur)[C::NVA], h8(&va_next)[C::NVA]) {
-        if constexpr (C::PV32)
-          pipe_iteration_pv32<C>(smem, vblk(j + 1), kblk(j + 3), s_in, s_out, p_in, p_out, ka_cur, ka_next, va_cur,
-                                 va_next, ws, lc);
-        else
-          pipe_steady<C>(smem, vblk(j), kblk(j + 3), s_in, s_out, p_in, p_out, ka_cur, ka_next, ws, lc);
-      };
       // steady state: the copies of the NBUF-4 tiles after u+3 may stay in
       // flight (the count is the smallest any wave issues, so waves with more
       // copies per tile wait a little longer than they must)
@@ -1091,20 +894,20 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
       // blocks the mirror image, so no registers are copied.
       int u = 0;
       for (; 2 * u + 4 < nb; ++u) {
-        steady(2 * u, sB, sA, pA, pB, kaA, kaB, vaA, vaB);
+        pipe_steady<C>(smem, vblk(2 * u), kblk(2 * u + 3), sB, sA, pA, pB, kaA, kaB, ws, lc);
         if (cp.issued >= u + C::NBUF)
           wait_vm(kSteadyWait);  // tile u+3 has landed
         else
           wait_vm(0);
         __syncthreads();  // ... everywhere; tile u is finished
         if (cp.issued < ntiles && cp.issued < u + 1 + C::NBUF) fast_issue<C>(p, smem, fc, cp, f, hd, wave, lc.lane);
-        steady(2 * u + 1, sA, sB, pB, pA, kaB, kaA, vaB, vaA);
+        pipe_steady<C>(smem, vblk(2 * u + 1), kblk(2 * u + 4), sA, sB, pB, pA, kaB, kaA, ws, lc);
       }
       __builtin_amdgcn_s_setprio(0);  // back to the default for the tail
       // Blocks 2u.. are left: four of them (every tile they need has landed
       // and no copy remains), or two when the sequence has only two tiles.
       if (nb - 2 * u == 4) {
-        steady(2 * u, sB, sA, pA, pB, kaA, kaB, vaA, vaB);
+        pipe_steady<C>(smem, vblk(2 * u), kblk(2 * u + 3), sB, sA, pA, pB, kaA, kaB, ws, lc);
         pipe_iteration<C, true, true, false>(smem, vblk(2 * u + 1), 0, sA, sB, pB, pA, kaB, kaA, ws, lc);
         u += 1;
       }
@@ -1133,11 +936,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
-      if constexpr (C::PV32) {
-        // row D of O^T: tile D/32, row m = D%32 sits in register 4(m/8) + m%4 of lane half (m%8)/4
-        constexpr int tl = C::D / 32, m = C::D % 32, rl = 4 * (m / 8) + m % 4, hl = (m % 8) / 4;
-        if (lc.h == hl) bad |= !(fabsf(ws.oacc32[qb][tl][rl]) <= 3.0e38f);
-      } else if constexpr (C::ONES) {
+      if constexpr (C::ONES) {
         constexpr int tl = C::D / 16, gl = (C::D % 16) / 4, rl = C::D % 4;
         if (lc.g == gl) {
 #pragma unroll
@@ -1160,7 +959,6 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
 
   if (p.nsplit > 1) {
     // ---- this split's partials: unnormalised O^T, offset and row sum per query ----
-    static_assert(!C::PV32, "key splits are dispatched for the 16-row PV layout only");
     const int64_t pbase = ((int64_t)(f * p.H + hd) * p.nsplit + split) * p.Lq;
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
@@ -1196,32 +994,6 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
 
   // ---- normalise and write O (fp16, round to nearest even) ----
   _Float16* ob = p.o + (int64_t)f * p.o_fs + (int64_t)hd * C::D;
-  if constexpr (C::PV32) {
-    // lane l holds query l%32 of each block: O^T rows 32t + 8j + 4h + 0..3 in
-    // registers 4j..4j+3 of tile t; the row sum (row D) lives in one lane half
-    constexpr int tl = C::D / 32, m = C::D % 32, rl = 4 * (m / 8) + m % 4, hl = (m % 8) / 4;
-#pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
-      const float l = __shfl(ws.oacc32[qb][tl][rl], 32 * hl + c32, 64);
-      const float inv = 1.0f / l;
-      const int row = qrow0 + 32 * qb + c32;
-      if (row < p.Lq) {
-#pragma unroll
-        for (int t = 0; t < C::NRT; ++t)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = 32 * t + 8 * j + 4 * lc.h;
-            if (col < C::D) {
-              h4 out;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) out[r] = (_Float16)(ws.oacc32[qb][t][4 * j + r] * inv);
-              *reinterpret_cast<h4*>(ob + (int64_t)row * p.o_ld + col) = out;
-            }
-          }
-      }
-    }
-    return;
-  }
 #pragma unroll
   for (int qb = 0; qb < C::NQB; ++qb) {
 #pragma unroll
@@ -1529,9 +1301,9 @@ void split_plan(int F, int Lq, int H, const int64_t* seg_len, int nseg, int& nsp
   }
 }
 
-template <int D, int NQB, int NKB, int NBUF, int MINB, bool PIPE, int W, bool PV32 = false>
+template <int D, int NQB, int NKB, int NBUF, int MINB, bool PIPE, int W>
 hipError_t launch_cfg(const KParams& kp, hipStream_t stream, float* workspace) {
-  using C = Cfg<D, NQB, NKB, NBUF, MINB, PIPE, W, PV32>;
+  using C = Cfg<D, NQB, NKB, NBUF, MINB, PIPE, W>;
   KParams p = kp;
   for (int i = 0; i < p.nseg; ++i)
     if (p.seg[i].ld * 2 * C::BN > 0x7fffffffLL) return hipErrorInvalidValue;  // 32-bit copy offsets
@@ -1610,11 +1382,7 @@ hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream) {
   }
   switch (a.d) {
     case 32: return launch_cfg<32, 2, 2, 4, 2, true, 4>(p, stream, nullptr);
-#if PL_D40_PV32
-    case 40: return launch_cfg<40, 2, 2, 4, 2, true, 4, true>(p, stream, nullptr);
-#else
     case 40: return launch_cfg<40, 2, 2, 4, 2, true, 4>(p, stream, nullptr);
-#endif
     case 80: return launch_cfg<80, 1, 2, 4, 1, true, 8>(p, stream, nullptr);
     case 160:
       if (a.Lq <= 64) return launch_cfg<160, 1, 2, 3, 1, false, 2>(p, stream, ws);
