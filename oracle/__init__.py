@@ -11,7 +11,9 @@ juhe.plus, "PersonaLive" for short, and the hysenlabs repository review):
 * ``attention``  -- reference-bank spatial self-attention
   (PersonaLive, section "三条条件通路" / three conditioning paths: the 16
   reference-layer features are concatenated with the denoiser's own K/V for
-  spatial self-attention).
+  spatial self-attention), and block-causal attention over a chunked
+  sequence (LPM write-up, section 6.3 分块因果注意力; the deep-compression-VAE
+  write-up: full attention inside a chunk, earlier chunks only across).
 * ``ddim``       -- the per-window DDIM step of the streaming pyramid
   (PersonaLive, sections "它解决什么" / specification and
   "流式金字塔去噪" / streaming pyramid denoising).
@@ -36,7 +38,7 @@ to each level) is a reading of a passage that does not state it: the
 arithmetic is pinned, the choice of content is "parity unpinned".
 """
 
-from .attention import refbank_attention, attend_rows, concat_segments
+from .attention import refbank_attention, attend_rows, concat_segments, chunk_causal_attention
 from .ddim import (
     sd_scaled_linear_alphas_cumprod,
     ddim_coefficients,
@@ -52,6 +54,7 @@ __all__ = [
     "refbank_attention",
     "attend_rows",
     "concat_segments",
+    "chunk_causal_attention",
     "sd_scaled_linear_alphas_cumprod",
     "ddim_coefficients",
     "ddim_step",

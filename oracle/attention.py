@@ -114,3 +114,40 @@ def refbank_attention(q, segments, heads, scale=None, frames=None, head_list=Non
             else:
                 out[f][:, cols] = o
     return out
+
+
+def chunk_causal_attention(q, self_kv, shared, heads, chunk_len, max_history=-1, scale=None):
+    """Block-causal attention over one token sequence per frame, in fp64.
+
+    Deep-compression-VAE write-up (papernotes) and LPM write-up, section 6.3
+    分块因果注意力: the sequence is cut into non-overlapping chunks of
+    ``chunk_len`` tokens; a token attends to every token of its own chunk and
+    of earlier chunks (at most ``max_history`` of them; negative = all), never
+    to a later chunk, and to the persistent reference tokens.
+
+    ``q``: [F, L, C]; ``self_kv``: (k, v) [F, L, C], row j of frame f in chunk
+    j // chunk_len; ``shared``: list of (k, v) [Ls, C] visible to every row.
+    Returns [F, L, C] fp64.  Plain definition: the visible keys of each row are
+    gathered and the row is attended with :func:`attend_rows`.
+    """
+    q = np.asarray(q)
+    F, L, C = q.shape
+    d = C // heads
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    ks, vs = (np.asarray(a, dtype=np.float64) for a in self_kv)
+    sk = [np.asarray(k, dtype=np.float64) for k, _ in shared]
+    sv = [np.asarray(v, dtype=np.float64) for _, v in shared]
+    out = np.empty((F, L, C), dtype=np.float64)
+    for f in range(F):
+        for r in range(L):
+            c = r // chunk_len
+            lo = 0 if max_history < 0 else max(0, c - max_history)
+            rows = np.arange(lo * chunk_len, min(L, (c + 1) * chunk_len))
+            kcat = np.concatenate([ks[f][rows]] + sk, axis=0)
+            vcat = np.concatenate([vs[f][rows]] + sv, axis=0)
+            qf = np.asarray(q[f][r:r + 1], dtype=np.float64)
+            for h in range(heads):
+                cols = slice(h * d, (h + 1) * d)
+                out[f, r, cols] = attend_rows(qf[:, cols], kcat[:, cols], vcat[:, cols], scale)[0]
+    return out

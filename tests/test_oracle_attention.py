@@ -245,3 +245,63 @@ def test_attend_rows_and_concat_helpers():
     assert np.array_equal(k[:3], segs[0][0][1]) and np.array_equal(k[3:], segs[1][0])
     o = attend_rows(np.zeros((1, 4)), k, v, 1.0)
     assert np.max(np.abs(o[0] - v.mean(axis=0))) <= 1e-12
+
+
+# ---- block-causal attention over a chunked sequence --------------------------------
+def _chunk_inputs(seed, F, L, C, n_shared=1, Ls=5):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((F, L, C))
+    kv = (rng.standard_normal((F, L, C)), rng.standard_normal((F, L, C)))
+    shared = [(rng.standard_normal((Ls, C)), rng.standard_normal((Ls, C))) for _ in range(n_shared)]
+    return q, kv, shared
+
+
+def test_chunk_causal_one_chunk_is_plain_attention():
+    # a chunk as long as the sequence (and unlimited history) masks nothing
+    from oracle import chunk_causal_attention
+    q, kv, shared = _chunk_inputs(1, 2, 7, 8)
+    got = chunk_causal_attention(q, kv, shared, 2, chunk_len=7)
+    segs = [(kv[0], kv[1], False)] + [(k, v, True) for k, v in shared]
+    assert np.allclose(got, refbank_attention(q, segs, 2), atol=1e-13)
+
+
+def test_chunk_causal_token_chunks_are_causal_sdpa():
+    # chunks of one token, no shared keys: textbook causal attention (library routine)
+    torch = pytest.importorskip("torch")
+    from oracle import chunk_causal_attention
+    q, kv, _ = _chunk_inputs(2, 1, 9, 6)
+    got = chunk_causal_attention(q, kv, [], 2, chunk_len=1)
+    tq, tk, tv = (torch.from_numpy(a[0].reshape(9, 2, 3).transpose(1, 0, 2).copy()) for a in (q, kv[0], kv[1]))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    assert np.allclose(got[0], ref.numpy().transpose(1, 0, 2).reshape(9, 6), atol=1e-13)
+
+
+def test_chunk_causal_brute_force_with_history_limit():
+    # each row by hand: its visible self keys are the chunks [c - H, c], plus the shared rows
+    from oracle import chunk_causal_attention
+    q, kv, shared = _chunk_inputs(3, 2, 11, 4, n_shared=2, Ls=3)
+    cl, hist = 3, 1
+    got = chunk_causal_attention(q, kv, shared, 1, chunk_len=cl, max_history=hist)
+    for f in range(2):
+        for r in range(11):
+            c = r // cl
+            keys = [j for j in range(11) if max(0, c - hist) <= j // cl <= c]
+            kk = np.concatenate([kv[0][f][keys]] + [k for k, _ in shared])
+            vv = np.concatenate([kv[1][f][keys]] + [v for _, v in shared])
+            s = kk @ q[f][r] / 2.0
+            w = [math.exp(x) for x in s]
+            want = sum(wi * vi for wi, vi in zip(w, vv)) / sum(w)
+            assert np.allclose(got[f, r], want, atol=1e-12)
+
+
+def test_chunk_causal_never_sees_later_chunks():
+    # changing a later chunk's keys and values leaves earlier rows unchanged
+    from oracle import chunk_causal_attention
+    q, kv, shared = _chunk_inputs(4, 1, 12, 4)
+    a = chunk_causal_attention(q, kv, shared, 1, chunk_len=4)
+    k2, v2 = kv[0].copy(), kv[1].copy()
+    k2[0, 8:] += 5.0
+    v2[0, 8:] -= 3.0
+    b = chunk_causal_attention(q, (k2, v2), shared, 1, chunk_len=4)
+    assert np.array_equal(a[0, :8], b[0, :8])
+    assert not np.allclose(a[0, 8:], b[0, 8:])
