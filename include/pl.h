@@ -113,6 +113,28 @@ pl_status pl_refbank_attn(const void* q, int64_t q_ld, int64_t q_frame_stride,
                           const pl_kv_segment* segs, int32_t nseg, float scale,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Block-causal attention over chunked sequences (several chunks' queries in
+ * one call).  LPM write-up, section 6.3 分块因果注意力, and the deep-compression-
+ * VAE write-up: a sequence is cut into non-overlapping chunks; a token attends
+ * to its own chunk and to earlier chunks (a limited number of them), never to
+ * a later one, and to the persistent reference tokens.
+ * For each frame, query row r belongs to chunk r / chunk_len.  Segment
+ * causal_seg holds the sequence's own keys and values, row j in chunk
+ * j / chunk_len (its len must equal Lq); row r sees its row j only if
+ * chunk(j) <= chunk(r) and chunk(r) - chunk(j) <= max_history (negative:
+ * unlimited).  Every other segment (reference tokens, sinks) is visible to
+ * every row.  Other arguments as pl_refbank_attn (single-pass kernels, no
+ * workspace).  The call checks every chunk's views before launching, then
+ * issues one launch per chunk over that chunk's rows and visible key range:
+ * nothing is copied.  PL_EINVAL additionally for causal_seg out of range,
+ * chunk_len < 1, a causal segment whose len is not Lq, or more than 65536
+ * chunks. */
+pl_status pl_refbank_attn_chunked(const void* q, int64_t q_ld, int64_t q_frame_stride,
+                                  void* o, int64_t o_ld, int64_t o_frame_stride,
+                                  int32_t F, int32_t Lq, int32_t H, int32_t d,
+                                  const pl_kv_segment* segs, int32_t nseg, int32_t causal_seg,
+                                  int32_t chunk_len, int32_t max_history, float scale, void* stream);
+
 /* pl_refbank_attn without a caller workspace, for callers that cannot
  * allocate device memory (code under graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, layout, results and

@@ -31,6 +31,7 @@ EXPORTED = (
     "pl_refbank_attn_workspace_size",
     "pl_refbank_attn",
     "pl_refbank_attn_noalloc",
+    "pl_refbank_attn_chunked",
     "pl_pyramid_ddim_step",
     "pl_pyramid_ddim_step_roll",
     "pl_sd_alphas_cumprod",
@@ -106,6 +107,9 @@ def load():
     lib.pl_refbank_attn_noalloc.restype = i32
     lib.pl_refbank_attn_noalloc.argtypes = [vp, i64, i64, vp, i64, i64, i32, i32, i32, i32,
                                             ctypes.POINTER(pl_kv_segment), i32, f32, vp]
+    lib.pl_refbank_attn_chunked.restype = i32
+    lib.pl_refbank_attn_chunked.argtypes = [vp, i64, i64, vp, i64, i64, i32, i32, i32, i32,
+                                            ctypes.POINTER(pl_kv_segment), i32, i32, i32, i32, f32, vp]
     lib.pl_pyramid_ddim_step.restype = i32
     lib.pl_pyramid_ddim_step.argtypes = [vp, vp, vp, vp, i32, i64, ctypes.POINTER(i32), i32,
                                          ctypes.POINTER(f64), i32, f64, i32, vp]
@@ -158,6 +162,10 @@ def pl_refbank_attn(*args):
 
 def pl_refbank_attn_noalloc(*args):
     return load().pl_refbank_attn_noalloc(*args)
+
+
+def pl_refbank_attn_chunked(*args):
+    return load().pl_refbank_attn_chunked(*args)
 
 
 def pl_refbank_attn_workspace_size(*args):
@@ -322,6 +330,39 @@ def refbank_attn(q, segments, heads, out=None, scale=None, stream=None, workspac
     st = pl_refbank_attn(ctypes.c_void_p(q.data_ptr()), q_ld, q_fs, ctypes.c_void_p(out.data_ptr()), o_ld, o_fs,
                          F, L, heads, d, segs, len(segments), float(scale), ws, ws_bytes, _stream_ptr(stream))
     _check("pl_refbank_attn", st)
+    return out
+
+
+def chunked_attn(q, self_kv, shared, heads, chunk_len, max_history=-1, out=None, scale=None, stream=None):
+    """Block-causal attention over chunked sequences (see ``pl_refbank_attn_chunked``).
+
+    ``q``: fp16 device ``[F, L, C]``; ``self_kv``: (k, v) ``[F, L, C]``, the
+    sequence's own keys (row j in chunk j // chunk_len); ``shared``: list of
+    (k, v) ``[Ls, C]`` visible to every row.  Returns ``out``.
+    """
+    _need(q, torch.float16, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [F, L, C]")
+    F, L, C = q.shape
+    if C % heads:
+        raise ValueError("C must be divisible by heads")
+    d = C // heads
+    if self_kv[0].dim() != 3 or tuple(self_kv[0].shape) != (F, L, C):
+        raise ValueError("the causal segment must be [F, L, C] like q")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, torch.float16, "out")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = d ** -0.5
+    q_ld, q_fs = _rows(q, "q")
+    o_ld, o_fs = _rows(out, "out")
+    segs, _keep = make_segments([tuple(self_kv)] + [tuple(kv) for kv in shared], F, C)
+    st = pl_refbank_attn_chunked(ctypes.c_void_p(q.data_ptr()), q_ld, q_fs, ctypes.c_void_p(out.data_ptr()), o_ld,
+                                 o_fs, F, L, heads, d, segs, len(segs), 0, int(chunk_len), int(max_history),
+                                 float(scale), _stream_ptr(stream))
+    _check("pl_refbank_attn_chunked", st)
     return out
 
 

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "pl_internal.h"
 
@@ -210,13 +211,14 @@ pl_status scratch_for_current_device(const char* fn, void** out) {
   return PL_OK;
 }
 
-// pl_refbank_attn and its allocation-free variant (noalloc: the key-split
-// partials go to the library's scratch; workspace arguments are unused).
-pl_status refbank_attn_impl(const char* fn, const void* q, int64_t q_ld, int64_t q_frame_stride, void* o,
-                            int64_t o_ld, int64_t o_frame_stride, int32_t F, int32_t Lq, int32_t H, int32_t d,
-                            const pl_kv_segment* segs, int32_t nseg, float scale, void* workspace,
-                            size_t workspace_bytes, bool noalloc, void* stream) {
-  (void)fn;
+// The checks of pl_refbank_attn and its variants; fills the launch
+// description (noalloc: the key-split partials go to the library's scratch;
+// workspace arguments are unused).
+pl_status validate_attn(const char* fn, const void* q, int64_t q_ld, int64_t q_frame_stride, void* o, int64_t o_ld,
+                        int64_t o_frame_stride, int32_t F, int32_t Lq, int32_t H, int32_t d,
+                        const pl_kv_segment* segs, int32_t nseg, float scale, void* workspace,
+                        size_t workspace_bytes, bool noalloc, pl::AttnLaunch* out) {
+  pl::AttnLaunch& a = *out;
   if (!q || !o) return fail(PL_EINVAL, "pl_refbank_attn: q and o must be non-null");
   if (!segs) return fail(PL_EINVAL, "pl_refbank_attn: segs must be non-null");
   if (F < 1 || Lq < 1 || H < 1) return fail(PL_EINVAL, "pl_refbank_attn: F, Lq, H must be >= 1 (got %d, %d, %d)", F, Lq, H);
@@ -235,7 +237,6 @@ pl_status refbank_attn_impl(const char* fn, const void* q, int64_t q_ld, int64_t
     return fail(PL_EUNSUPPORTED, "pl_refbank_attn: strides must be multiples of 8 elements");
   if (!aligned16(q) || !aligned16(o)) return fail(PL_EUNSUPPORTED, "pl_refbank_attn: q and o must be 16-byte aligned");
   int64_t total = 0;
-  pl::AttnLaunch a;
   std::memset(&a, 0, sizeof(a));
   for (int i = 0; i < nseg; ++i) {
     const pl_kv_segment& s = segs[i];
@@ -297,6 +298,17 @@ pl_status refbank_attn_impl(const char* fn, const void* q, int64_t q_ld, int64_t
   a.d = d;
   a.nseg = nseg;
   a.scale = scale;
+  return PL_OK;
+}
+
+pl_status refbank_attn_impl(const char* fn, const void* q, int64_t q_ld, int64_t q_frame_stride, void* o,
+                            int64_t o_ld, int64_t o_frame_stride, int32_t F, int32_t Lq, int32_t H, int32_t d,
+                            const pl_kv_segment* segs, int32_t nseg, float scale, void* workspace,
+                            size_t workspace_bytes, bool noalloc, void* stream) {
+  pl::AttnLaunch a;
+  if (pl_status st = validate_attn(fn, q, q_ld, q_frame_stride, o, o_ld, o_frame_stride, F, Lq, H, d, segs, nseg,
+                                   scale, workspace, workspace_bytes, noalloc, &a))
+    return st;
   return device_status(pl::launch_refbank_attn(a, static_cast<hipStream_t>(stream)), "pl_refbank_attn launch");
 }
 
@@ -310,6 +322,56 @@ pl_status pl_refbank_attn(const void* q, int64_t q_ld, int64_t q_frame_stride, v
                           size_t workspace_bytes, void* stream) {
   return refbank_attn_impl("pl_refbank_attn", q, q_ld, q_frame_stride, o, o_ld, o_frame_stride, F, Lq, H, d, segs,
                            nseg, scale, workspace, workspace_bytes, false, stream);
+}
+
+pl_status pl_refbank_attn_chunked(const void* q, int64_t q_ld, int64_t q_frame_stride, void* o, int64_t o_ld,
+                                  int64_t o_frame_stride, int32_t F, int32_t Lq, int32_t H, int32_t d,
+                                  const pl_kv_segment* segs, int32_t nseg, int32_t causal_seg, int32_t chunk_len,
+                                  int32_t max_history, float scale, void* stream) {
+  const char* fn = "pl_refbank_attn_chunked";
+  if (!segs) return fail(PL_EINVAL, "%s: segs must be non-null", fn);
+  if (nseg < 1 || nseg > PL_MAX_SEGMENTS)
+    return fail(PL_EINVAL, "%s: nseg must be in [1, %d] (got %d)", fn, PL_MAX_SEGMENTS, nseg);
+  if (causal_seg < 0 || causal_seg >= nseg)
+    return fail(PL_EINVAL, "%s: causal_seg must be in [0, nseg) (got %d)", fn, causal_seg);
+  if (Lq < 1 || chunk_len < 1) return fail(PL_EINVAL, "%s: Lq and chunk_len must be >= 1 (got %d, %d)", fn, Lq, chunk_len);
+  if (segs[causal_seg].len != Lq)
+    return fail(PL_EINVAL, "%s: the causal segment must hold the Lq = %d rows of the queries' sequence (got %lld)", fn,
+                Lq, (long long)segs[causal_seg].len);
+  const int nchunks = (Lq + chunk_len - 1) / chunk_len;
+  if (nchunks > 65536) return fail(PL_EINVAL, "%s: more than 65536 chunks (one launch each)", fn);
+  // the whole call first (every view at its full extent), then each chunk's
+  // launch: all checks run before anything is launched
+  pl::AttnLaunch whole;
+  if (pl_status st = validate_attn(fn, q, q_ld, q_frame_stride, o, o_ld, o_frame_stride, F, Lq, H, d, segs, nseg,
+                                   scale, nullptr, 0, false, &whole))
+    return st;
+  std::vector<pl::AttnLaunch> launches((size_t)nchunks);
+  for (int c = 0; c < nchunks; ++c) {
+    const int64_t r0 = (int64_t)c * chunk_len;
+    const int rows = (int)std::min<int64_t>(chunk_len, Lq - r0);
+    const int64_t lo = max_history < 0 ? 0 : std::max<int64_t>(0, c - (int64_t)max_history);
+    const int64_t k0 = lo * chunk_len, k1 = std::min<int64_t>(Lq, r0 + chunk_len);
+    pl_kv_segment cs[PL_MAX_SEGMENTS];
+    for (int i = 0; i < nseg; ++i) cs[i] = segs[i];
+    pl_kv_segment& sc = cs[causal_seg];
+    sc.k = static_cast<const char*>(sc.k) + k0 * sc.ld * 2;
+    sc.v = static_cast<const char*>(sc.v) + k0 * sc.ld * 2;
+    sc.len = k1 - k0;
+    const void* qc = static_cast<const char*>(q) + r0 * q_ld * 2;
+    void* oc = static_cast<char*>(o) + r0 * o_ld * 2;
+    if (pl_status st = validate_attn(fn, qc, q_ld, q_frame_stride, oc, o_ld, o_frame_stride, F, rows, H, d, cs, nseg,
+                                     scale, nullptr, 0, false, &launches[(size_t)c])) {
+      char msg[512];
+      std::snprintf(msg, sizeof(msg), "%s", g_last_error);
+      return fail(st, "%s (chunk %d)", msg, c);
+    }
+  }
+  for (int c = 0; c < nchunks; ++c) {
+    const hipError_t e = pl::launch_refbank_attn(launches[(size_t)c], static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PL_EDEVICE, "%s: launch of chunk %d: %s", fn, c, hipGetErrorString(e));
+  }
+  return ok();
 }
 
 pl_status pl_refbank_attn_noalloc(const void* q, int64_t q_ld, int64_t q_frame_stride, void* o, int64_t o_ld,

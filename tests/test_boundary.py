@@ -343,3 +343,22 @@ def test_noalloc_rejects_split_beyond_its_scratch(lib):
     # argument checks are those of pl_refbank_attn
     assert B.pl_refbank_attn_noalloc(None, C, L * C, ctypes.c_void_p(0x60000000), C, L * C, F, L, H, 160, segs, 5,
                                      0.08, None) == B.PL_EINVAL
+
+
+def test_chunked_rejects(lib):
+    # (fake addresses, never dereferenced; every case fails validation)
+    F, L, C, H = 2, 100, 64, 2
+    q, o = ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000)
+    ok = _segs((ctypes.c_void_p(0x3000000), ctypes.c_void_p(0x4000000), L, C, L * C),
+               (ctypes.c_void_p(0x5000000), ctypes.c_void_p(0x6000000), 7, C, 0))
+    def call(segs=ok, nseg=2, causal=0, cl=32, hist=-1, Lq=L, q_=q, o_=o):
+        return B.pl_refbank_attn_chunked(q_, C, Lq * C, o_, C, Lq * C, F, Lq, H, 32, segs, nseg, causal, cl, hist,
+                                         0.17, None)
+    assert call(causal=2) == B.PL_EINVAL and "causal_seg" in B.last_error()
+    assert call(causal=-1) == B.PL_EINVAL
+    assert call(cl=0) == B.PL_EINVAL
+    assert call(Lq=99) == B.PL_EINVAL and "Lq" in B.last_error()  # the causal segment holds 100 rows
+    assert call(q_=None) == B.PL_EINVAL
+    assert call(o_=ctypes.c_void_p(0x3000000)) == B.PL_EINVAL and "overlaps" in B.last_error()
+    assert call(segs=None) == B.PL_EINVAL
+    assert call(nseg=9) == B.PL_EINVAL
