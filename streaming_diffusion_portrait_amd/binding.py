@@ -16,7 +16,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpl.so")
+# PL_LIBRARY names another build of the same library (the host-sanitizer build)
+LIB_PATH = os.environ.get("PL_LIBRARY") or os.path.join(_HERE, "libpl.so")
 
 PL_OK, PL_EINVAL, PL_EUNSUPPORTED, PL_EDEVICE = 0, 1, 2, 3
 PL_MAX_SEGMENTS = 8
