@@ -15,13 +15,42 @@
 // 64 features x 64 rows (2 x 2 products per 16-wide step, the operands of the
 // next kPrefetch steps in flight); a workgroup of 4 waves owns 64 features x
 // 256 rows.
-// Workgroups run feature tiles fastest and the ids dealt round-robin to the 8
-// XCDs are remapped to contiguous ranges, so the feature tiles of the same
-// rows share one L2 and x is read from HBM once.
+// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2; the
+// ids are remapped so that each XCD works through a compact block of output
+// tiles (tile_of below), which it reads x and W for through that L2.
+#include <cmath>
+
 #include "pl_internal.h"
 
 namespace pl {
 namespace {
+
+// Workgroup -> output tile (row tile mt, feature tile nt).  blockIdx.x goes to
+// XCD blockIdx.x % 8, so the ids are first remapped to one contiguous range
+// per XCD (XCD x holds total / 8 of them, one more for the first total % 8).
+// In that order the tiles run in groups of gm row tiles, row tiles fastest:
+// the tiles one XCD holds form a block of about gm row tiles by share / gm
+// feature tiles, whose x rows and W rows are what its L2 has to fetch.
+__device__ __forceinline__ void tile_of(int total, int m_tiles, int n_tiles, int gm, int64_t& mt, int& nt) {
+  const int b = blockIdx.x, x = b & 7, q = total >> 3, rem = total & 7;
+  const int lid = (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + (b >> 3);
+  const int gsz = gm * n_tiles;
+  const int g = lid / gsz, r = lid - g * gsz;
+  const int first = g * gm, ge = min(gm, m_tiles - first);
+  mt = first + r % ge;
+  nt = r / ge;
+}
+
+// The group height that makes an XCD's block cheapest to fetch: with P tiles
+// per XCD as a x (P / a) tiles of bm rows and bn features, the bytes are
+// proportional to a bm + (P / a) bn, least at a = sqrt(P bn / bm).
+int group_rows(int64_t m_tiles, int n_tiles, int bm, int bn) {
+  const double share = (double)(m_tiles * n_tiles + 7) / 8.0;
+  int a = (int)std::lround(std::sqrt(share * bn / bm));
+  if (a < 1) a = 1;
+  if (a > m_tiles) a = (int)m_tiles;
+  return a;
+}
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -51,14 +80,14 @@ __device__ __forceinline__ void load_step(const LinearLaunch& p, int64_t nrow0, 
 }
 
 template <int PF>
-__global__ void __launch_bounds__(64 * kWaves, 2) linear_kernel(LinearLaunch p, int n_tiles, int total) {
+__global__ void __launch_bounds__(64 * kWaves, 2)
+    linear_kernel(LinearLaunch p, int m_tiles, int n_tiles, int total, int gm) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
-  int lid = blockIdx.x;
-  if ((total & 7) == 0) lid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int nt = lid % n_tiles;
-  const int64_t mt = lid / n_tiles;
+  int64_t mt;
+  int nt;
+  tile_of(total, m_tiles, n_tiles, gm, mt, nt);
   const int64_t n0 = (int64_t)nt * kTileN;
   const int64_t m0 = mt * kTileM + (int64_t)wave * kTileMW;
 
@@ -193,16 +222,16 @@ __device__ __forceinline__ int so(int row, int c) {
 }
 
 template <class G, bool LDS_OUT>
-__global__ void __launch_bounds__(G::THREADS, G::MINW) linear_staged_kernel(LinearLaunch p, int n_tiles, int total) {
+__global__ void __launch_bounds__(G::THREADS, G::MINW)
+    linear_staged_kernel(LinearLaunch p, int m_tiles, int n_tiles, int total, int gm) {
   __shared__ __attribute__((aligned(16))) char smem[G::LDS];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave / G::WF, wf = wave % G::WF;
   const int lane = tid & 63, h = lane >> 5, c32 = lane & 31;
-  int lid = blockIdx.x;
-  if ((total & 7) == 0) lid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int nt = lid % n_tiles;
-  const int64_t mt = lid / n_tiles;
+  int64_t mt;
+  int nt;
+  tile_of(total, m_tiles, n_tiles, gm, mt, nt);
   const int64_t n0 = (int64_t)nt * G::BN;
   const int64_t mw0 = mt * G::BM;  // workgroup's first row
 
@@ -365,19 +394,23 @@ __global__ void __launch_bounds__(G::THREADS, G::MINW) linear_staged_kernel(Line
   }
 }
 
+// gm = 0 picks the group height by group_rows
 template <class G>
-hipError_t launch_staged(const LinearLaunch& a, hipStream_t stream) {
+hipError_t launch_staged(const LinearLaunch& a, hipStream_t stream, int gm = 0) {
   static_assert(G::BM * G::BN * 2 <= G::LDS, "the output tile fits in the stage buffers");
   const int n_tiles = a.N / G::BN;
-  const int64_t total = ((a.M + G::BM - 1) / G::BM) * n_tiles;
+  const int64_t m_tiles = (a.M + G::BM - 1) / G::BM;
+  const int64_t total = m_tiles * n_tiles;
   if (total > 0x7fffffff) return hipErrorInvalidValue;
+  if (gm <= 0) gm = group_rows(m_tiles, n_tiles, G::BM, G::BN);
+  if (gm > m_tiles) gm = (int)m_tiles;
   // 16-byte row stores need y 16-byte aligned with a row pitch of 8 elements
   if ((reinterpret_cast<uintptr_t>(a.y) & 15) == 0 && a.y_ld % 8 == 0)
-    hipLaunchKernelGGL((linear_staged_kernel<G, true>), dim3((unsigned)total), dim3(G::THREADS), 0, stream, a, n_tiles,
-                       (int)total);
+    hipLaunchKernelGGL((linear_staged_kernel<G, true>), dim3((unsigned)total), dim3(G::THREADS), 0, stream, a,
+                       (int)m_tiles, n_tiles, (int)total, gm);
   else
-    hipLaunchKernelGGL((linear_staged_kernel<G, false>), dim3((unsigned)total), dim3(G::THREADS), 0, stream, a, n_tiles,
-                       (int)total);
+    hipLaunchKernelGGL((linear_staged_kernel<G, false>), dim3((unsigned)total), dim3(G::THREADS), 0, stream, a,
+                       (int)m_tiles, n_tiles, (int)total, gm);
   return hipGetLastError();
 }
 
@@ -389,18 +422,23 @@ hipError_t launch_linear(const LinearLaunch& a, hipStream_t stream) {
     // UNet levels): 256 x 256 tiles where K is long and they still give about
     // one workgroup per CU (the contraction-bound case; 8 waves of 64 x 128,
     // two per SIMD, hide the operand reads that one wave per SIMD could not);
-    // 128 x 192 where N
-    // allows and M is large enough for 1024+ of them (the fused q/k/v
-    // weights: x is read through L2 a third as often as with 64-wide tiles,
-    // and 5 operand reads feed 6 products); 256 x 64 where M is large enough
-    // for 1024+ of those; 128 x 64 otherwise.
+    // 128 x 128 with three stages in flight where K is long and those give
+    // one workgroup per CU (the rows are few, so each workgroup streams a
+    // long slice of W: the deeper pipeline covers its fetch latency);
+    // 128 x 192 where N allows and M is large enough for 1024+ of them (the
+    // fused q/k/v weights: x is read through L2 a third as often as with
+    // 64-wide tiles, and 5 operand reads feed 6 products); 256 x 64 where M
+    // is large enough for 1024+ of those; 128 x 64 otherwise.
     using Square = GemmCfg<4, 2, 4, 2, 8>;
+    using Deep = GemmCfg<2, 2, 2, 3, 4>;
     using Wide = GemmCfg<2, 2, 3, 2>;
     using Tall = GemmCfg<4, 2, 2, 2>;
     using Base = GemmCfg<4, 1, 2, 2>;
     auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * (a.N / bn); };
     if (a.K >= 1024 && a.N % Square::BN == 0 && tiles(Square::BM, Square::BN) >= 224)
       return launch_staged<Square>(a, stream);
+    if (a.K >= 1024 && a.N % Deep::BN == 0 && tiles(Deep::BM, Deep::BN) >= 192 && tiles(Deep::BM, Deep::BN) <= 256)
+      return launch_staged<Deep>(a, stream);
     if (a.N % Wide::BN == 0 && tiles(Wide::BM, Wide::BN) >= 1024) return launch_staged<Wide>(a, stream);
     if (tiles(Tall::BM, Tall::BN) >= 1024) return launch_staged<Tall>(a, stream);
     return launch_staged<Base>(a, stream);
@@ -409,11 +447,13 @@ hipError_t launch_linear(const LinearLaunch& a, hipStream_t stream) {
   const int64_t m_tiles = (a.M + kTileM - 1) / kTileM;
   const int64_t total = m_tiles * n_tiles;
   if (total > 0x7fffffff) return hipErrorInvalidValue;
+  const int gm = group_rows(m_tiles, n_tiles, kTileM, kTileN);
   if (a.K % (16 * kPrefetch) == 0)
-    hipLaunchKernelGGL(linear_kernel<kPrefetch>, dim3((unsigned)total), dim3(64 * kWaves), 0, stream, a, n_tiles,
-                       (int)total);
+    hipLaunchKernelGGL(linear_kernel<kPrefetch>, dim3((unsigned)total), dim3(64 * kWaves), 0, stream, a, (int)m_tiles,
+                       n_tiles, (int)total, gm);
   else
-    hipLaunchKernelGGL(linear_kernel<1>, dim3((unsigned)total), dim3(64 * kWaves), 0, stream, a, n_tiles, (int)total);
+    hipLaunchKernelGGL(linear_kernel<1>, dim3((unsigned)total), dim3(64 * kWaves), 0, stream, a, (int)m_tiles, n_tiles,
+                       (int)total, gm);
   return hipGetLastError();
 }
 

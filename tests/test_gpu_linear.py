@@ -43,7 +43,9 @@ def check(got, ref, K):
 
 
 SMALL = [("ragged rows", 300, 128, 48, True), ("one row", 1, 64, 16, False), ("clip kv", 1, 640, 768, False),
-         ("expression kv", 32 * 16, 640, 16, False), ("wide", 77, 1280, 1280, True), ("many tiles", 1000, 192, 320, False)]
+         ("expression kv", 32 * 16, 640, 16, False), ("wide", 77, 1280, 1280, True), ("many tiles", 1000, 192, 320, False),
+         # 84 tiles of 128 x 64 (not a multiple of the 8 XCDs), grouped 2 row tiles high
+         ("odd tile count", 1500, 448, 256, True)]
 
 
 @pytest.mark.parametrize("name,M,N,K,bias", SMALL, ids=[c[0] for c in SMALL])
@@ -57,9 +59,10 @@ def test_linear_full_compare(B, name, M, N, K, bias):
 
 # Shapes that select each tile configuration of the K % 64 == 0 kernel
 # (128 x 64, 256 x 64 for large M, 128 x 192 for large M with N a multiple of
-# 192, 256 x 256 for long K), with ragged row tails.
+# 192, 256 x 256 for long K, 128 x 128 with three stages for long K and few
+# rows), with ragged row tails.
 TILES = [("128x64 tiles", 333, 128, 128), ("256x64 tiles", 16300, 1024, 128), ("128x192 tiles", 16300, 1920, 640),
-         ("256x256 tiles", 3600, 3840, 1024)]
+         ("256x256 tiles", 3600, 3840, 1024), ("128x128 3-stage tiles", 1000, 3840, 1024)]
 
 
 @pytest.mark.parametrize("row_stores", [True, False], ids=["row stores", "direct stores"])
