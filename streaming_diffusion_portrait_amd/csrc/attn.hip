@@ -139,6 +139,12 @@ struct Cfg {
   static_assert(PLB % 16 == 0, "planes hold 16-byte chunks");
   static_assert(NBUF >= 2 && NBUF <= 6, "ring of 2 to 6 buffers");
   static_assert(NI * (NBUF - 1) <= 48, "vmcnt wait table range");
+  // the pass-end flags: their own bytes when the first tile's fast-path
+  // decision needs them while the ring is in use (ones column), else the last
+  // ring slot, which a following pass fills only after its first barrier
+  static constexpr int FLAGS_AT = ONES ? LDSB : (NBUF - 1) * BUFB;
+  static constexpr int SMEM = ONES ? LDSB + 4 * W : LDSB;
+  static_assert(ONES || 4 * W <= BUFB, "flags fit in a ring slot");
 };
 
 struct KParams {
@@ -340,6 +346,17 @@ struct LaneCtx {
   int krow_off;     // K operand LDS byte offset within a 32-key block (plane 0)
   int vrow_off[2];  // V^T operand LDS byte offsets of the two transposing reads (planes 0, 1)
 };
+
+// K step st: lane half h reads plane 2st+h at key c32.  V^T read r of lane
+// (g, c16): key vrow(g) + 16r + c16/4, dims 4(c16%4)..+3 of the 16-dim tile,
+// i.e. plane 2t + (c16%4)/2, byte 8*(c16%2) of the key's chunk.
+template <class C>
+__device__ __forceinline__ void lane_offsets(LaneCtx& lc) {
+  lc.krow_off = (lc.lane & 31) * 16 + lc.h * C::PLB;
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    lc.vrow_off[r] = (vrow(lc.g) + 16 * r + (lc.c16 >> 2)) * 16 + ((lc.c16 & 3) >> 1) * C::PLB + 8 * (lc.c16 & 1);
+}
 
 // K operands of one 32-key block: step st reads planes 2st (lanes 0..31)
 // and 2st+1 (lanes 32..63); the padding column D, if any, lies in the
@@ -694,8 +711,8 @@ __device__ __forceinline__ void pipe_steady(const char* smem, int vblk, int kblk
 
 template <class C>
 __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[C::LDSB];
-  __shared__ int flags[C::W];
+  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+  int* const flags = reinterpret_cast<int*>(smem + C::FLAGS_AT);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -750,17 +767,11 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
       *reinterpret_cast<h8*>(smem + i * C::TILEB + C::CPR * C::PLB + 16 * lc.lane) = one;
     }
   }
-  // K step st: lane half h reads plane 2st+h at key c32.  V^T read r of lane
-  // (g, c16): key vrow(g) + 16r + c16/4, dims 4(c16%4)..+3 of the 16-dim tile,
-  // i.e. plane 2t + (c16%4)/2, byte 8*(c16%2) of the key's chunk.
   if constexpr (C::RSUM) {  // A of the row-sum products: row 0 (lanes with l % 16 == 0) all ones
     const _Float16 a1 = lc.c16 == 0 ? (_Float16)1.0f : (_Float16)0.0f;
     ws.onesA = (h8){a1, a1, a1, a1, a1, a1, a1, a1};
   }
-  lc.krow_off = c32 * 16 + lc.h * C::PLB;
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-    lc.vrow_off[r] = (vrow(lc.g) + 16 * r + (lc.c16 >> 2)) * 16 + ((lc.c16 & 3) >> 1) * C::PLB + 8 * (lc.c16 & 1);
+  lane_offsets<C>(lc);
 
   // Tiles in the key sequence (this split's range of them) and this wave's
   // copy instructions per tile.
@@ -887,16 +898,15 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
         if (2 < nb) load_k<C>(smem, kblk(2), lc, kaA);
       }
       // steady state: the copies of the NBUF-4 tiles after u+3 may stay in
-      // flight (the count is the smallest any wave issues, so waves with more
-      // copies per tile wait a little longer than they must)
-      constexpr int kSteadyWait = (2 * C::LI / C::W) * (C::NBUF - 4);
+      // flight (this wave's own count: the waves issue 2 or 3 copies a tile)
+      const int steady_wait = cp.ni * (C::NBUF - 4);
       // Even blocks read (sB -> pB, sA <- S^T, pA into PV, K into kaB), odd
       // blocks the mirror image, so no registers are copied.
       int u = 0;
       for (; 2 * u + 4 < nb; ++u) {
         pipe_steady<C>(smem, vblk(2 * u), kblk(2 * u + 3), sB, sA, pA, pB, kaA, kaB, ws, lc);
         if (cp.issued >= u + C::NBUF)
-          wait_vm(kSteadyWait);  // tile u+3 has landed
+          wait_vm(steady_wait);  // tile u+3 has landed
         else
           wait_vm(0);
         __syncthreads();  // ... everywhere; tile u is finished
@@ -1100,10 +1110,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
       *reinterpret_cast<h8*>(smem + i * C::TILEB + C::CPR * C::PLB + 16 * lc.lane) = one;
     }
   }
-  lc.krow_off = c32 * 16 + lc.h * C::PLB;
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-    lc.vrow_off[r] = (vrow(lc.g) + 16 * r + (lc.c16 >> 2)) * 16 + ((lc.c16 & 3) >> 1) * C::PLB + 8 * (lc.c16 & 1);
+  lane_offsets<C>(lc);
 
   // the whole key sequence is one (possibly ragged) tile
   Copier<C> cp;
@@ -1332,6 +1339,12 @@ hipError_t launch_cfg(const KParams& kp, hipStream_t stream, float* workspace) {
   return hipGetLastError();
 }
 
+// d = 80: query blocks per wave, key blocks per tile, ring buffers, workgroups
+// per CU, pipelined fast tiles, waves per workgroup
+#ifndef PL_D80_CFG
+#define PL_D80_CFG 1, 2, 4, 1, true, 8
+#endif
+
 // d = 160 configurations: 4 waves of 32 query rows, or 2 for frames of at most 64 rows
 using Cfg160 = Cfg<160, 1, 2, 3, 1, false, 4>;
 using Cfg160s = Cfg<160, 1, 2, 3, 1, false, 2>;
@@ -1383,7 +1396,7 @@ hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream) {
   switch (a.d) {
     case 32: return launch_cfg<32, 2, 2, 4, 2, true, 4>(p, stream, nullptr);
     case 40: return launch_cfg<40, 2, 2, 4, 2, true, 4>(p, stream, nullptr);
-    case 80: return launch_cfg<80, 1, 2, 4, 1, true, 8>(p, stream, nullptr);
+    case 80: return launch_cfg<80, PL_D80_CFG>(p, stream, nullptr);
     case 160:
       if (a.Lq <= 64) return launch_cfg<160, 1, 2, 3, 1, false, 2>(p, stream, ws);
       return launch_cfg<160, 1, 2, 3, 1, false, 4>(p, stream, ws);
