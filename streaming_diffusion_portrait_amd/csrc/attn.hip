@@ -104,7 +104,7 @@ __device__ __forceinline__ int vrow(int g) { return 8 * (g & 1) + 4 * (g >> 1); 
 #define PL_PLANE_PAD 64
 #endif
 
-template <int D_, int NQB_, int NKB_, int NBUF_, int MINB_, bool PIPE_, int W_>
+template <int D_, int NQB_, int NKB_, int NBUF_, int MINB_, bool PIPE_, int W_, int DSPLIT_ = 1>
 struct Cfg {
   static constexpr int D = D_;
   static constexpr int W = W_;                // wavefronts per workgroup
@@ -115,9 +115,15 @@ struct Cfg {
   static constexpr int NBUF = NBUF_;          // LDS tile buffers in the ring
   static constexpr int MINB = MINB_;          // workgroups per CU the register budget is sized for
   static constexpr int BN = 32 * NKB;         // keys per tile
-  static constexpr int QWG = 32 * NQB * W;     // query rows per workgroup
+  // DSPLIT waves share each query block, each holding NDT / DSPLIT of the
+  // O^T d tiles (all of them compute the block's S^T and softmax): fewer
+  // registers per wave, so more waves per SIMD
+  static constexpr int DSPLIT = DSPLIT_;
+  static constexpr int WQ = W / DSPLIT;        // waves with distinct query blocks
+  static constexpr int QWG = 32 * NQB * WQ;    // query rows per workgroup
   static constexpr int KST = (D + 15) / 16;   // 16-wide contraction steps of S^T
   static constexpr int NDT = (D + 15) / 16;   // 16-row tiles of O^T
+  static constexpr int NDW = NDT / DSPLIT_;   // ... held by one wave
   static constexpr bool ONES = (D % 16) != 0; // padding column D carries ones / -m
   // no ones column (d = 32, 80, 160): the row sums come from two more PV
   // products per query block with a constant A whose first row is ones (with
@@ -138,6 +144,8 @@ struct Cfg {
   static_assert(BN == 64, "one plane per load instruction: 64 keys of 16 bytes");
   static_assert(PLB % 16 == 0, "planes hold 16-byte chunks");
   static_assert(NBUF >= 2 && NBUF <= 6, "ring of 2 to 6 buffers");
+  static_assert(W % DSPLIT == 0 && NDT % DSPLIT == 0, "waves and d tiles split evenly");
+  static_assert(DSPLIT == 1 || RSUM, "with a d split every wave needs the row sums: no ones column");
   static_assert(NI * (NBUF - 1) <= 48, "vmcnt wait table range");
   // the pass-end flags: their own bytes when the first tile's fast-path
   // decision needs them while the ring is in use (ones column), else the last
@@ -333,7 +341,8 @@ __device__ __forceinline__ void fast_issue(const KParams& p, char* smem, FastCop
 template <class C>
 struct WaveState {
   h8 qf[C::NQB][C::KST];       // Q^T operands (scaled, fp16)
-  f4 oacc[C::NQB][2][C::NDT];  // O^T accumulators: [query block][16-query half][16-row d tile]
+  f4 oacc[C::NQB][2][C::NDW];  // O^T accumulators: [query block][16-query half][16-row d tile, from dt0]
+  int dt0;                     // first O^T d tile of this wave
   float mrun[C::NQB];          // running offset of query l%32 of each block
   f16v negm[C::NQB];           // -mrun in every accumulator slot: the seed of fast S^T products (no ones column)
   f4 osum[C::NQB][2];          // RSUM: row 0 holds the row sums of the half's 16 queries
@@ -394,11 +403,11 @@ __device__ __forceinline__ void qk_block(const char* smem, int kblk, const WaveS
 
 // V^T operands of one 32-key block.
 template <class C>
-__device__ __forceinline__ void load_vt(const char* smem, int vblk, const LaneCtx& lc, h8 (&va)[C::NDT]) {
+__device__ __forceinline__ void load_vt(const char* smem, int vblk, const LaneCtx& lc, int dt0, h8 (&va)[C::NDW]) {
 #pragma unroll
-  for (int t = 0; t < C::NDT; ++t) {
-    const int a0 = vblk + 2 * t * C::PLB + lc.vrow_off[0];
-    const int a1 = vblk + 2 * t * C::PLB + lc.vrow_off[1];
+  for (int t = 0; t < C::NDW; ++t) {
+    const int a0 = vblk + 2 * (dt0 + t) * C::PLB + lc.vrow_off[0];
+    const int a1 = vblk + 2 * (dt0 + t) * C::PLB + lc.vrow_off[1];
     const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(smem + a0));
     const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(smem + a1));
     u4 w;
@@ -412,11 +421,11 @@ __device__ __forceinline__ void load_vt(const char* smem, int vblk, const LaneCt
 
 // O^T += V^T P^T for one 32-key block.
 template <class C>
-__device__ __forceinline__ void pv_block(const h8 (&va)[C::NDT], const h8 (&pb)[C::NQB][2], WaveState<C>& ws) {
+__device__ __forceinline__ void pv_block(const h8 (&va)[C::NDW], const h8 (&pb)[C::NQB][2], WaveState<C>& ws) {
 #pragma unroll
   for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
-    for (int t = 0; t < C::NDT; ++t)
+    for (int t = 0; t < C::NDW; ++t)
 #pragma unroll
       for (int grp = 0; grp < 2; ++grp)
         ws.oacc[qb][grp][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t], pb[qb][grp], ws.oacc[qb][grp][t], 0, 0, 0);
@@ -515,7 +524,7 @@ __device__ __forceinline__ void rescale_acc(WaveState<C>& ws, const LaneCtx& lc,
     for (int grp = 0; grp < 2; ++grp) {
       const float a = __shfl(alpha[qb], 16 * grp + lc.c16, 64);
 #pragma unroll
-      for (int t = 0; t < C::NDT; ++t) ws.oacc[qb][grp][t] *= a;
+      for (int t = 0; t < C::NDW; ++t) ws.oacc[qb][grp][t] *= a;
       if constexpr (C::RSUM) ws.osum[qb][grp] *= a;
     }
 }
@@ -529,8 +538,8 @@ __device__ __forceinline__ void tile_step(const char* smem, int kt, int valid, b
     if (kb > 0 && valid <= 32 * kb) break;  // a tile's last block holds no key (short segments)
     f16v s[C::NQB];
     qk_block<C, FAST && !C::ONES>(smem, kt + kb * C::KBLK, ws, lc, s);
-    h8 va[C::NDT];
-    load_vt<C>(smem, kt + C::TILEB + kb * C::KBLK, lc, va);
+    h8 va[C::NDW];
+    load_vt<C>(smem, kt + C::TILEB + kb * C::KBLK, lc, ws.dt0, va);
     h8 pb[C::NQB][2];
     float alpha[C::NQB];
     bool resc;
@@ -551,7 +560,7 @@ __device__ __forceinline__ void sched_iteration() {
   // registers) threaded with the softmax's vector work; then the reads of the
   // next K operands (into the registers those products just read) and the PV
   // products with the rest of the vector work
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * C::NDT, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * C::NDW, 0);
 #pragma unroll
   for (int i = 0; i < C::NQB * C::KST; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
@@ -559,7 +568,7 @@ __device__ __forceinline__ void sched_iteration() {
   }
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::KST, 0);
 #pragma unroll
-  for (int i = 0; i < C::NQB * 2 * C::NDT; ++i) {
+  for (int i = 0; i < C::NQB * 2 * C::NDW; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedValu, PL_SCHED_PER, 0);
   }
@@ -624,14 +633,14 @@ __device__ __forceinline__ void pipe_iteration_fixed(const char* smem, int vblk,
                                                      f16v (&s_out)[C::NQB], const h8 (&p_in)[C::NQB][2],
                                                      h8 (&p_out)[C::NQB][2], const h8 (&ka_cur)[C::KST],
                                                      h8 (&ka_next)[C::KST], WaveState<C>& ws, const LaneCtx& lc) {
-  constexpr int NQK = C::KST * C::NQB, NPV = (C::NDT + (C::RSUM ? 1 : 0)) * C::NQB * 2, NM = NQK + NPV;
+  constexpr int NQK = C::KST * C::NQB, NPV = (C::NDW + (C::RSUM ? 1 : 0)) * C::NQB * 2, NM = NQK + NPV;
   constexpr int NV = sm_ops<C>() * C::NQB;
   // vector instructions after each S^T / PV product (d = 40: tuned; otherwise
   // 4 after each S^T product and the rest spread over the PV products)
   constexpr int SQK = C::ONES ? PL_SLOT_QK : 4;
   constexpr int SPV = C::ONES ? PL_SLOT_PV : (NV - NQK * SQK + NPV - 1) / NPV;
-  h8 va[C::NDT];
-  load_vt<C>(smem, vblk, lc, va);
+  h8 va[C::NDW];
+  load_vt<C>(smem, vblk, lc, ws.dt0, va);
   load_k<C>(smem, kblk3, lc, ka_next);
   __builtin_amdgcn_sched_barrier(0);
   FastSoftmax<C> sm;
@@ -652,7 +661,7 @@ __device__ __forceinline__ void pipe_iteration_fixed(const char* smem, int vblk,
           ka_cur[st], ws.qf[qb][st], st > 0 ? s_out[qb] : C::ONES ? (f16v){} : ws.negm[qb], 0, 0, 0);
     } else {  // O^T += V^T(b) P^T(b): d tiles outermost (the V reads land in that order), then the row sums
       const int i = m - NQK, t = i / (2 * C::NQB), qb = (i / 2) % C::NQB, grp = i % 2;
-      if (t < C::NDT)
+      if (t < C::NDW)
         ws.oacc[qb][grp][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t], p_in[qb][grp], ws.oacc[qb][grp][t], 0, 0, 0);
       else
         ws.osum[qb][grp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ws.onesA, p_in[qb][grp], ws.osum[qb][grp], 0, 0, 0);
@@ -685,8 +694,8 @@ __device__ __forceinline__ void pipe_iteration(const char* smem, int vblk, int k
                                                h8 (&ka_next)[C::KST], WaveState<C>& ws, const LaneCtx& lc) {
   float alpha[C::NQB];
   bool resc;
-  h8 va[C::NDT];
-  load_vt<C>(smem, vblk, lc, va);
+  h8 va[C::NDW];
+  load_vt<C>(smem, vblk, lc, ws.dt0, va);
   if (QK) qk_regs<C, !C::ONES>(ka_cur, ws, s_out);  // pipelined blocks are fast
   if (SM) softmax_block<C, false>(s_in, ws, lc, 32, false, p_out, alpha, resc);
   if (KR) load_k<C>(smem, kblk3, lc, ka_next);  // after the products read ka_cur
@@ -733,9 +742,10 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
   const int rem = lid - hd * (p.F * p.nqt);
   const int f = rem / p.nqt;
   const int qt = rem - f * p.nqt;
-  const int qrow0 = qt * C::QWG + wave * 32 * C::NQB;
+  const int qrow0 = qt * C::QWG + (wave % C::WQ) * 32 * C::NQB;
 
   WaveState<C> ws;
+  ws.dt0 = C::DSPLIT == 1 ? 0 : (wave / C::WQ) * C::NDW;
   // Q^T operands: Q * scale * log2(e) rounded to fp16, zero beyond d and beyond Lq.
   {
     const _Float16* qb_ = p.q + (int64_t)f * p.q_fs + (int64_t)hd * C::D;
@@ -822,7 +832,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
 #pragma unroll
       for (int grp = 0; grp < 2; ++grp)
 #pragma unroll
-        for (int t = 0; t < C::NDT; ++t) ws.oacc[qb][grp][t] = (f4){0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < C::NDW; ++t) ws.oacc[qb][grp][t] = (f4){0.f, 0.f, 0.f, 0.f};
       if constexpr (C::RSUM) ws.osum[qb][0] = ws.osum[qb][1] = (f4){0.f, 0.f, 0.f, 0.f};
       if constexpr (C::ONES) if (lc.h) ws.qf[qb][C::KST - 1][0] = (_Float16)0.0f;  // offset column: none yet
     }
@@ -987,11 +997,11 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
           const bool empty = ntiles <= 0;
           float* po = p.part_o + (pbase + row) * C::D;
 #pragma unroll
-          for (int t = 0; t < C::NDT; ++t) {
-            const int col = 16 * t + 4 * lc.g;
+          for (int t = 0; t < C::NDW; ++t) {
+            const int col = 16 * (ws.dt0 + t) + 4 * lc.g;
             if (col < C::D) *reinterpret_cast<f4*>(po + col) = empty ? (f4){0.f, 0.f, 0.f, 0.f} : ws.oacc[qb][grp][t];
           }
-          if (lc.g == 0) {
+          if (lc.g == 0 && ws.dt0 == 0) {
             float* pm = p.part_ml + (pbase + row) * 2;
             pm[0] = empty ? -INFINITY : mo;
             pm[1] = empty ? 0.f : l;
@@ -1019,8 +1029,8 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
       const int row = qrow0 + 32 * qb + 16 * grp + lc.c16;
       if (row < p.Lq) {
 #pragma unroll
-        for (int t = 0; t < C::NDT; ++t) {
-          const int col = 16 * t + 4 * lc.g;
+        for (int t = 0; t < C::NDW; ++t) {
+          const int col = 16 * (ws.dt0 + t) + 4 * lc.g;
           if (col < C::D) {
             h4 out;
 #pragma unroll
@@ -1078,7 +1088,7 @@ struct ShortStage {
 
 template <class C>
 __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams p, int nsplit) {
-  static_assert(C::NQB == 1, "one 32-query block per step");
+  static_assert(C::NQB == 1 && C::DSPLIT == 1, "one 32-query block per step, all d tiles in each wave");
   using S = ShortStage<C>;
   __shared__ __attribute__((aligned(16))) char smem[S::LDS];
 
@@ -1147,6 +1157,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
   __syncthreads();  // the K/V tile (and the constant plane) and the first Q block are in LDS
 
   WaveState<C> ws;
+  ws.dt0 = 0;
   if constexpr (C::RSUM) {  // A of the row-sum products: row 0 (lanes with l % 16 == 0) all ones
     const _Float16 a1 = lc.c16 == 0 ? (_Float16)1.0f : (_Float16)0.0f;
     ws.onesA = (h8){a1, a1, a1, a1, a1, a1, a1, a1};
@@ -1173,7 +1184,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp) {
 #pragma unroll
-      for (int t = 0; t < C::NDT; ++t) ws.oacc[0][grp][t] = (f4){0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < C::NDW; ++t) ws.oacc[0][grp][t] = (f4){0.f, 0.f, 0.f, 0.f};
       if constexpr (C::RSUM) ws.osum[0][grp] = (f4){0.f, 0.f, 0.f, 0.f};
     }
     tile_step<C, false>(smem, 0, valid, true, ws, lc);
@@ -1191,7 +1202,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
       const float inv = 1.0f / l;
       const int row = 16 * grp + lc.c16;
 #pragma unroll
-      for (int t = 0; t < C::NDT; ++t) {
+      for (int t = 0; t < C::NDW; ++t) {
         const int col = 16 * t + 4 * lc.g;
         if (col < C::D) {
           h4 out;
@@ -1308,9 +1319,9 @@ void split_plan(int F, int Lq, int H, const int64_t* seg_len, int nseg, int& nsp
   }
 }
 
-template <int D, int NQB, int NKB, int NBUF, int MINB, bool PIPE, int W>
+template <int D, int NQB, int NKB, int NBUF, int MINB, bool PIPE, int W, int DSPLIT = 1>
 hipError_t launch_cfg(const KParams& kp, hipStream_t stream, float* workspace) {
-  using C = Cfg<D, NQB, NKB, NBUF, MINB, PIPE, W>;
+  using C = Cfg<D, NQB, NKB, NBUF, MINB, PIPE, W, DSPLIT>;
   KParams p = kp;
   for (int i = 0; i < p.nseg; ++i)
     if (p.seg[i].ld * 2 * C::BN > 0x7fffffffLL) return hipErrorInvalidValue;  // 32-bit copy offsets
@@ -1345,9 +1356,13 @@ hipError_t launch_cfg(const KParams& kp, hipStream_t stream, float* workspace) {
 #define PL_D80_CFG 1, 2, 4, 1, true, 8
 #endif
 
-// d = 160 configurations: 4 waves of 32 query rows, or 2 for frames of at most 64 rows
+// d = 160 configurations: 4 waves of 32 query rows; for frames of at most 64
+// rows, 2 query blocks with 2 waves each, each wave holding half of O^T's d
+// tiles (one wave per SIMD either way: the split halves each wave's PV chain,
+// 20.3 -> 16.4 us at the 8^2 level; at 16^2, where 8 such waves would share the
+// SIMDs two by two, the repeated S^T work costs more: 54.5 -> 62.5 us)
 using Cfg160 = Cfg<160, 1, 2, 3, 1, false, 4>;
-using Cfg160s = Cfg<160, 1, 2, 3, 1, false, 2>;
+using Cfg160s = Cfg<160, 1, 2, 3, 1, false, 4, 2>;
 
 }  // namespace
 
@@ -1398,7 +1413,7 @@ hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream) {
     case 40: return launch_cfg<40, 2, 2, 4, 2, true, 4>(p, stream, nullptr);
     case 80: return launch_cfg<80, PL_D80_CFG>(p, stream, nullptr);
     case 160:
-      if (a.Lq <= 64) return launch_cfg<160, 1, 2, 3, 1, false, 2>(p, stream, ws);
+      if (a.Lq <= 64) return launch_cfg<160, 1, 2, 3, 1, false, 4, 2>(p, stream, ws);
       return launch_cfg<160, 1, 2, 3, 1, false, 4>(p, stream, ws);
     default: return hipErrorInvalidValue;
   }

@@ -56,6 +56,9 @@ SMALL = [
     ("d80 ragged NT2", 80, 2, 1030, 1, [(1030, False), (70, True)], 1.0),
     ("d160 ragged NT1", 160, 2, 70, 2, [(70, False), (33, True)], 1.0),
     ("d160 ragged NT2", 160, 1, 1025, 1, [(1025, False), (31, True), (32, True)], 1.0),
+    # frames of at most 64 rows: two waves per query block, each with half of O^T's d tiles
+    ("d160 small frame ragged", 160, 3, 37, 2, [(37, False), (100, True), (1, True)], 1.0),
+    ("d160 small frame whole tiles", 160, 2, 64, 2, [(64, False), (128, True), (64, True)], 1.0),
     ("d32 ragged", 32, 2, 257, 2, [(257, False), (256, True), (5, True)], 1.0),
     ("d32 NT4", 32, 1, 1024, 2, [(1024, False), (1024, True)], 1.0),
     ("single key", 40, 2, 64, 2, [(1, False)], 1.0),
