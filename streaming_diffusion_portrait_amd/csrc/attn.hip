@@ -742,7 +742,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
   const int rem = lid - hd * (p.F * p.nqt);
   const int f = rem / p.nqt;
   const int qt = rem - f * p.nqt;
-  const int qrow0 = qt * C::QWG + (wave % C::WQ) * 32 * C::NQB;
+  const int qrow0 = qt * C::QWG + (C::DSPLIT == 1 ? wave : wave % C::WQ) * 32 * C::NQB;
 
   WaveState<C> ws;
   ws.dt0 = C::DSPLIT == 1 ? 0 : (wave / C::WQ) * C::NDW;

@@ -36,20 +36,33 @@ motion_min_l2_kernel(const float* __restrict__ query, const float* __restrict__ 
   double part[PL_MAX_MOTION_BANK];
 #pragma unroll
   for (int j = 0; j < PL_MAX_MOTION_BANK; ++j) part[j] = 0.0;
-  // Every entry slot is read without a branch (slots past n re-read the last
-  // entry; their sums are ignored) and the loop is unrolled, so the loads of 8
-  // strides (all of a 512-d embedding) are in flight together instead of one
-  // memory round trip per load.
+  // Every entry slot and element is read without a branch (slots past n
+  // re-read the last entry, whose sums are ignored).  The elements are taken
+  // in batches of 8 strides (all of a 512-d embedding): a batch's fp32 loads
+  // all go out before any of them is used, so they share one memory round
+  // trip, and only then are they widened and accumulated in fp64.
   const float* brow[PL_MAX_MOTION_BANK];
 #pragma unroll
   for (int j = 0; j < PL_MAX_MOTION_BANK; ++j) brow[j] = bank + (int64_t)min(j, n - 1) * D;
-#pragma unroll 8
-  for (int k = lane; k < D; k += kWave) {
-    const double qv = q[k];
+  constexpr int kStrides = 8;
+  for (int k0 = 0; k0 < D; k0 += kWave * kStrides) {
+    float qf[kStrides], bf[PL_MAX_MOTION_BANK][kStrides];
+    // (elements beyond D are read at D-1 and their differences set to zero)
 #pragma unroll
-    for (int j = 0; j < PL_MAX_MOTION_BANK; ++j) {
-      const double diff = qv - (double)brow[j][k];
-      part[j] = fma(diff, diff, part[j]);
+    for (int s = 0; s < kStrides; ++s) {
+      const int k = min(k0 + s * kWave + lane, D - 1);
+      qf[s] = q[k];
+#pragma unroll
+      for (int j = 0; j < PL_MAX_MOTION_BANK; ++j) bf[j][s] = brow[j][k];
+    }
+#pragma unroll
+    for (int s = 0; s < kStrides; ++s) {
+      const bool in = k0 + s * kWave + lane < D;
+#pragma unroll
+      for (int j = 0; j < PL_MAX_MOTION_BANK; ++j) {
+        const double diff = in ? (double)qf[s] - (double)bf[j][s] : 0.0;
+        part[j] = fma(diff, diff, part[j]);
+      }
     }
   }
   double best = 0.0;
