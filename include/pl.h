@@ -39,7 +39,7 @@ typedef struct pl_pile pl_pile;  /* the latents pile's state machine (defined be
 #define PL_EUNSUPPORTED 2  /* valid in principle but not implemented (head dim, alignment) */
 #define PL_EDEVICE 3       /* the HIP runtime reported an error at launch */
 
-#define PL_ABI_VERSION 4
+#define PL_ABI_VERSION 5
 #define PL_MAX_SEGMENTS 8       /* key segments per attention call: self + reference + anchors (5 used) */
 #define PL_MAX_WINDOWS 8        /* windows per pile (the pages use 4) */
 #define PL_MAX_MOTION_BANK 4    /* reference embedding + at most 3 anchors */
@@ -152,6 +152,24 @@ pl_status pl_refbank_attn_noalloc(const void* q, int64_t q_ld, int64_t q_frame_s
                                   void* o, int64_t o_ld, int64_t o_frame_stride,
                                   int32_t F, int32_t Lq, int32_t H, int32_t d,
                                   const pl_kv_segment* segs, int32_t nseg, float scale, void* stream);
+
+/* Bounds report of a checking build: for whoever changes the attention
+ * kernels' indexing (no page defines it).  A library built with
+ * PL_DEBUG_BOUNDS checks every global and LDS access of the attention kernels
+ * (pl_refbank_attn and its variants, the short-context and key-split paths)
+ * against the extent of the buffer it belongs to before making it; a failed
+ * check sets one bit of a device-wide mask and the access is skipped.  Bits:
+ * 0 K/V copy source, 1 K/V copy destination (LDS), 2 Q load, 3 O store,
+ * 4 and 5 key-split partials, 6 and 7 K and V^T operand reads (LDS),
+ * 8 to 11 short context (Q copy source and destination, O store, block
+ * buffer), 12 and 13 key-split merge (partials read, O store).
+ *   mask   out: the bits set since the last reset (0: every access stayed in
+ *          its buffer).
+ *   reset  non-zero: clear the mask after reading it.
+ * Synchronises the current device (blocking copies of the mask).  Builds
+ * without the checks write 0 and return PL_EUNSUPPORTED; PL_EINVAL if mask
+ * is NULL; PL_EDEVICE on a HIP error. */
+pl_status pl_debug_bounds(uint64_t* mask, int32_t reset);
 
 /* ------------------------------------------------------------------------ *
  * Projections either side of the attention

@@ -33,6 +33,7 @@ EXPORTED = (
     "pl_refbank_attn",
     "pl_refbank_attn_noalloc",
     "pl_refbank_attn_chunked",
+    "pl_debug_bounds",
     "pl_pyramid_ddim_step",
     "pl_pyramid_ddim_step_roll",
     "pl_sd_alphas_cumprod",
@@ -108,6 +109,8 @@ def load():
     lib.pl_refbank_attn_noalloc.restype = i32
     lib.pl_refbank_attn_noalloc.argtypes = [vp, i64, i64, vp, i64, i64, i32, i32, i32, i32,
                                             ctypes.POINTER(pl_kv_segment), i32, f32, vp]
+    lib.pl_debug_bounds.restype = i32
+    lib.pl_debug_bounds.argtypes = [ctypes.POINTER(ctypes.c_uint64), i32]
     lib.pl_refbank_attn_chunked.restype = i32
     lib.pl_refbank_attn_chunked.argtypes = [vp, i64, i64, vp, i64, i64, i32, i32, i32, i32,
                                             ctypes.POINTER(pl_kv_segment), i32, i32, i32, i32, f32, vp]
@@ -293,6 +296,17 @@ def _workspace(F, L, heads, d, segs, device, workspace=None):
     if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
         raise TypeError("workspace must be a contiguous device tensor")
     return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), workspace
+
+
+def debug_bounds(reset=True):
+    """Mask of attention access sites that failed their bounds check (see
+    ``pl_debug_bounds``); None when the loaded library has no checks."""
+    mask = ctypes.c_uint64(0)
+    st = load().pl_debug_bounds(ctypes.byref(mask), 1 if reset else 0)
+    if st == PL_EUNSUPPORTED:
+        return None
+    _check("pl_debug_bounds", st)
+    return int(mask.value)
 
 
 def workspace_size(F, L, heads, d, seg_lens):

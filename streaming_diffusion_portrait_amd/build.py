@@ -9,6 +9,10 @@ links one shared library next to this file; it always recompiles.
 UndefinedBehaviorSanitizer on the host code only (device code is built as
 usual).  It is for CPU runs of the argument checks; load it with the ASan
 runtime preloaded and ``PL_LIBRARY`` pointing at it.
+
+``--debug-bounds`` builds ``libpl_dbg.so``: the attention kernels with a
+bounds check before every global and LDS access (``pl_debug_bounds`` reads
+which access sites failed); load it through ``PL_LIBRARY``.
 """
 
 import concurrent.futures
@@ -22,6 +26,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpl.so")
 SAN_LIB = os.path.join(HERE, "libpl_san.so")
+DBG_LIB = os.path.join(HERE, "libpl_dbg.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -65,14 +70,15 @@ def _compile(hipcc, src, objdir, extra):
     return obj, msgs
 
 
-def build(verbose=False, sanitize=False, lib_path=None, obj_dir=None):
+def build(verbose=False, sanitize=False, lib_path=None, obj_dir=None, debug_bounds=False):
     """Compile every csrc/*.hip for gfx950 and link libpl.so (libpl_san.so with
-    ``sanitize``), or ``lib_path`` with objects under ``obj_dir``; returns the
-    library's path."""
+    ``sanitize``, libpl_dbg.so with ``debug_bounds``), or ``lib_path`` with
+    objects under ``obj_dir``; returns the library's path."""
     hipcc = _hipcc()
-    objdir = obj_dir or (os.path.join(OBJ, "san") if sanitize else OBJ)
-    extra = SAN_FLAGS if sanitize else []
-    lib = lib_path or (SAN_LIB if sanitize else LIB)
+    variant = "san" if sanitize else "dbg" if debug_bounds else None
+    objdir = obj_dir or (os.path.join(OBJ, variant) if variant else OBJ)
+    extra = (SAN_FLAGS if sanitize else []) + (["-DPL_DEBUG_BOUNDS"] if debug_bounds else [])
+    lib = lib_path or (SAN_LIB if sanitize else DBG_LIB if debug_bounds else LIB)
     os.makedirs(objdir, exist_ok=True)
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
@@ -93,4 +99,4 @@ def build(verbose=False, sanitize=False, lib_path=None, obj_dir=None):
 
 
 if __name__ == "__main__":
-    build(verbose="-q" not in sys.argv, sanitize="--sanitize" in sys.argv)
+    build(verbose="-q" not in sys.argv, sanitize="--sanitize" in sys.argv, debug_bounds="--debug-bounds" in sys.argv)

@@ -168,7 +168,48 @@ struct KParams {
   int nsplit, tps;
   float* part_o;  // [F*H*nsplit][Lq][D] fp32
   float* part_ml; // [F*H*nsplit][Lq][2] fp32: offset (log2 units), row sum
+#ifdef PL_DEBUG_BOUNDS
+  // elements from q, o and each segment's k (and v) to one past the last one
+  // the call may touch; floats of part_o
+  int64_t q_ext, o_ext, seg_ext[PL_MAX_SEGMENTS], part_ext;
+#endif
 };
+
+// ---- bounds-checking build ------------------------------------------------------
+// Built with PL_DEBUG_BOUNDS, every global and LDS access of the attention
+// kernels is first checked against the extent of the buffer it belongs to; a
+// failed check sets bit `site` of a device-wide mask (read back by
+// pl_debug_bounds) and the access is skipped, so a wrong index is reported
+// instead of touching memory the call does not own.  Other builds compile the
+// checks away (the condition is not even evaluated).
+enum BoundsSite {
+  kSiteKvSrc = 0,   // K/V tile copy: global source
+  kSiteKvDst,       // K/V tile copy: LDS destination
+  kSiteQLoad,       // Q operands
+  kSiteOStore,      // O rows
+  kSitePartO,       // key split: partial O
+  kSitePartMl,      // key split: offset and row sum
+  kSiteLdsK,        // K operand reads from LDS
+  kSiteLdsV,        // V^T operand reads from LDS
+  kSiteShortQSrc,   // short context: Q block copy, global source
+  kSiteShortQDst,   // short context: Q block copy, LDS destination
+  kSiteShortO,      // short context: O rows
+  kSiteShortBuf,    // short context: block buffer in LDS
+  kSiteCombineIn,   // key split merge: partials read
+  kSiteCombineOut,  // key split merge: O rows
+};
+#ifdef PL_DEBUG_BOUNDS
+__device__ unsigned long long g_bounds_mask;
+__device__ __forceinline__ bool bounds_ok(bool ok, int site) {
+  if (!ok) atomicOr(&g_bounds_mask, 1ull << site);
+  return ok;
+}
+#define PL_BOUNDS(ok, site) bounds_ok((ok), (site))
+#else
+#define PL_BOUNDS(ok, site) true
+#endif
+// [off, off + n) inside [0, ext)
+#define PL_IN(off, n, ext) ((int64_t)(off) >= 0 && (int64_t)(off) + (int64_t)(n) <= (int64_t)(ext))
 
 __device__ __forceinline__ unsigned pack_h2(float a, float b) {
   h2 v = {(_Float16)a, (_Float16)b};
@@ -230,6 +271,9 @@ struct Copier {
   int64_t off;  // its first key within the segment
   int issued;   // tiles copied so far
   int ni;       // copy instructions this wave issues per tile
+#ifdef PL_DEBUG_BOUNDS
+  unsigned lds_end;  // LDS byte address one past the kernel's shared memory
+#endif
 };
 
 #pragma clang diagnostic push
@@ -272,7 +316,10 @@ __device__ __forceinline__ void issue_tile(const KParams& p, char* smem, Copier<
     if (u < 2 * C::LI) {
       const bool isv = u >= C::LI;
       const int pl = isv ? u - C::LI : u;
-      lds_dma16(buf + (isv ? C::TILEB : 0) + pl * C::PLB, voff, (isv ? vbase : kbase) + 16 * pl);
+      const unsigned dst = buf + (isv ? C::TILEB : 0) + pl * C::PLB;
+      if (PL_BOUNDS(!__any(!PL_IN(base + voff / 2 + 8 * pl, 8, p.seg_ext[cp.s])), kSiteKvSrc) &&
+          PL_BOUNDS(dst + 1024u <= cp.lds_end, kSiteKvDst))
+        lds_dma16(dst, voff, (isv ? vbase : kbase) + 16 * pl);
     }
   }
   cp.off += C::BN;
@@ -328,7 +375,13 @@ __device__ __forceinline__ void fast_issue(const KParams& p, char* smem, FastCop
     if (u < 2 * C::LI) {
       const bool isv = u >= C::LI;
       const int pl = isv ? u - C::LI : u;
-      lds_dma16(buf + (isv ? C::TILEB : 0) + pl * C::PLB, fc.voff, (isv ? fc.vp : fc.kp) + 16 * pl);
+      const unsigned dst = buf + (isv ? C::TILEB : 0) + pl * C::PLB;
+      if (PL_BOUNDS(!__any(!PL_IN(((isv ? fc.vp : fc.kp) - reinterpret_cast<const char*>(isv ? p.seg[fc.s].v : p.seg[fc.s].k)) / 2 +
+                                      fc.voff / 2 + 8 * pl,
+                                  8, p.seg_ext[fc.s])),
+                    kSiteKvSrc) &&
+          PL_BOUNDS(dst + 1024u <= cp.lds_end, kSiteKvDst))
+        lds_dma16(dst, fc.voff, (isv ? fc.vp : fc.kp) + 16 * pl);
     }
   }
   fc.kp += fc.step;
@@ -354,6 +407,9 @@ struct LaneCtx {
   int lane, h, c16, g;
   int krow_off;     // K operand LDS byte offset within a 32-key block (plane 0)
   int vrow_off[2];  // V^T operand LDS byte offsets of the two transposing reads (planes 0, 1)
+#ifdef PL_DEBUG_BOUNDS
+  int lds_bytes;    // the kernel's shared memory
+#endif
 };
 
 // K step st: lane half h reads plane 2st+h at key c32.  V^T read r of lane
@@ -373,8 +429,10 @@ __device__ __forceinline__ void lane_offsets(LaneCtx& lc) {
 template <class C>
 __device__ __forceinline__ void load_k(const char* smem, int kblk, const LaneCtx& lc, h8 (&ka)[C::KST]) {
 #pragma unroll
-  for (int st = 0; st < C::KST; ++st)
-    ka[st] = *reinterpret_cast<const h8*>(smem + kblk + lc.krow_off + 2 * st * C::PLB);
+  for (int st = 0; st < C::KST; ++st) {
+    const int a = kblk + lc.krow_off + 2 * st * C::PLB;
+    ka[st] = PL_BOUNDS(PL_IN(a, 16, lc.lds_bytes), kSiteLdsK) ? *reinterpret_cast<const h8*>(smem + a) : (h8){};
+  }
 }
 
 // S^T = K Q^T for every query block of the wave, from K operands in registers.
@@ -406,8 +464,9 @@ template <class C>
 __device__ __forceinline__ void load_vt(const char* smem, int vblk, const LaneCtx& lc, int dt0, h8 (&va)[C::NDW]) {
 #pragma unroll
   for (int t = 0; t < C::NDW; ++t) {
-    const int a0 = vblk + 2 * (dt0 + t) * C::PLB + lc.vrow_off[0];
-    const int a1 = vblk + 2 * (dt0 + t) * C::PLB + lc.vrow_off[1];
+    int a0 = vblk + 2 * (dt0 + t) * C::PLB + lc.vrow_off[0];
+    int a1 = vblk + 2 * (dt0 + t) * C::PLB + lc.vrow_off[1];
+    if (!PL_BOUNDS(!__any(!(PL_IN(a0, 8, lc.lds_bytes) && PL_IN(a1, 8, lc.lds_bytes))), kSiteLdsV)) a0 = a1 = 0;
     const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(smem + a0));
     const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(smem + a1));
     u4 w;
@@ -756,7 +815,9 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
       for (int st = 0; st < C::KST; ++st) {
         const int col = 16 * st + 8 * lc.h;
         h8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (row < p.Lq && col < C::D) {
+        if (row < p.Lq && col < C::D &&
+            PL_BOUNDS(PL_IN((int64_t)f * p.q_fs + (int64_t)row * p.q_ld + (int64_t)hd * C::D + col, 8, p.q_ext),
+                      kSiteQLoad)) {
           const h8 x = *reinterpret_cast<const h8*>(qb_ + (int64_t)row * p.q_ld + col);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = (_Float16)((float)x[e] * p.c2);
@@ -782,6 +843,9 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
     ws.onesA = (h8){a1, a1, a1, a1, a1, a1, a1, a1};
   }
   lane_offsets<C>(lc);
+#ifdef PL_DEBUG_BOUNDS
+  lc.lds_bytes = C::SMEM;
+#endif
 
   // Tiles in the key sequence (this split's range of them) and this wave's
   // copy instructions per tile.
@@ -804,6 +868,9 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
     t -= nts;
   }
   Copier<C> cp;
+#ifdef PL_DEBUG_BOUNDS
+  cp.lds_end = lds_addr(smem) + (unsigned)C::SMEM;
+#endif
   cp.ni = 0;
 #pragma unroll
   for (int j = 0; j < C::NI; ++j) cp.ni += (wave + C::W * j < 2 * C::LI) ? 1 : 0;
@@ -999,9 +1066,11 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
 #pragma unroll
           for (int t = 0; t < C::NDW; ++t) {
             const int col = 16 * (ws.dt0 + t) + 4 * lc.g;
-            if (col < C::D) *reinterpret_cast<f4*>(po + col) = empty ? (f4){0.f, 0.f, 0.f, 0.f} : ws.oacc[qb][grp][t];
+            if (col < C::D && PL_BOUNDS(PL_IN((pbase + row) * C::D + col, 4, p.part_ext), kSitePartO))
+              *reinterpret_cast<f4*>(po + col) = empty ? (f4){0.f, 0.f, 0.f, 0.f} : ws.oacc[qb][grp][t];
           }
-          if (lc.g == 0 && ws.dt0 == 0) {
+          if (lc.g == 0 && ws.dt0 == 0 &&
+              PL_BOUNDS(PL_IN((pbase + row) * 2, 2, p.part_ext / C::D * 2), kSitePartMl)) {
             float* pm = p.part_ml + (pbase + row) * 2;
             pm[0] = empty ? -INFINITY : mo;
             pm[1] = empty ? 0.f : l;
@@ -1031,7 +1100,9 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) refbank_attn_kernel(KPara
 #pragma unroll
         for (int t = 0; t < C::NDW; ++t) {
           const int col = 16 * (ws.dt0 + t) + 4 * lc.g;
-          if (col < C::D) {
+          if (col < C::D &&
+              PL_BOUNDS(PL_IN((int64_t)f * p.o_fs + (int64_t)row * p.o_ld + (int64_t)hd * C::D + col, 4, p.o_ext),
+                        kSiteOStore)) {
             h4 out;
 #pragma unroll
             for (int r = 0; r < 4; ++r) out[r] = (_Float16)(ws.oacc[qb][grp][t][r] * inv);
@@ -1121,9 +1192,15 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
     }
   }
   lane_offsets<C>(lc);
+#ifdef PL_DEBUG_BOUNDS
+  lc.lds_bytes = S::LDS;
+#endif
 
   // the whole key sequence is one (possibly ragged) tile
   Copier<C> cp;
+#ifdef PL_DEBUG_BOUNDS
+  cp.lds_end = lds_addr(smem) + (unsigned)S::LDS;
+#endif
   cp.s = 0;
   cp.off = 0;
   cp.issued = 0;
@@ -1146,8 +1223,13 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
 #pragma unroll
     for (int j = 0; j < S::NQI; ++j) {
       const int r = j * S::RPI + qrow;
-      if (lc.lane < S::RPI * S::CPRQ && r < 32)
-        lds_dma16(dst + j * S::RPI * S::CPRQ * 16, (unsigned)(min(r, last) * p.q_ld * 2 + 16 * qchunk), src);
+      const unsigned voff = (unsigned)(min(r, last) * p.q_ld * 2 + 16 * qchunk);
+      const unsigned d = dst + j * S::RPI * S::CPRQ * 16;
+      if (lc.lane < S::RPI * S::CPRQ && r < 32 &&
+          PL_BOUNDS(PL_IN((int64_t)f * p.q_fs + (int64_t)hd * C::D + (int64_t)(32 * blk) * p.q_ld + voff / 2, 8, p.q_ext),
+                    kSiteShortQSrc) &&
+          PL_BOUNDS(d + 16u * (unsigned)(S::RPI * S::CPRQ) <= cp.lds_end, kSiteShortQDst))
+        lds_dma16(d, voff, src);
     }
   };
 
@@ -1176,7 +1258,8 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
     for (int st = 0; st < C::KST; ++st) {
       const int col = 16 * st + 8 * lc.h;
       h8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (col < C::D) x = *reinterpret_cast<const h8*>(buf + c32 * (2 * C::D) + 2 * col);
+      if (col < C::D && PL_BOUNDS(PL_IN((buf - smem) + c32 * (2 * C::D) + 2 * col, 16, S::LDS), kSiteShortBuf))
+        x = *reinterpret_cast<const h8*>(buf + c32 * (2 * C::D) + 2 * col);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ws.qf[0][st][e] = (_Float16)((float)x[e] * p.c2);
     }
@@ -1204,7 +1287,7 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
 #pragma unroll
       for (int t = 0; t < C::NDW; ++t) {
         const int col = 16 * t + 4 * lc.g;
-        if (col < C::D) {
+        if (col < C::D && PL_BOUNDS(PL_IN((buf - smem) + row * (2 * C::D) + 2 * col, 8, S::LDS), kSiteShortBuf)) {
           h4 out;
 #pragma unroll
           for (int r = 0; r < 4; ++r) out[r] = (_Float16)(ws.oacc[0][grp][t][r] * inv);
@@ -1216,7 +1299,11 @@ __global__ void __launch_bounds__(C::THREADS, C::MINB) short_ctx_kernel(KParams 
 #pragma unroll
     for (int j = 0; j < S::NQI; ++j) {
       const int r = j * S::RPI + qrow;
-      if (lc.lane < S::RPI * S::CPRQ && r < 32 && 32 * blk + r < p.Lq)
+      if (lc.lane < S::RPI * S::CPRQ && r < 32 && 32 * blk + r < p.Lq &&
+          PL_BOUNDS(PL_IN((buf - smem) + r * (2 * C::D) + 16 * qchunk, 16, S::LDS), kSiteShortBuf) &&
+          PL_BOUNDS(PL_IN((int64_t)f * p.o_fs + (int64_t)hd * C::D + (int64_t)(32 * blk + r) * p.o_ld + 8 * qchunk, 8,
+                          p.o_ext),
+                    kSiteShortO))
         *reinterpret_cast<h8*>(ob + (int64_t)(32 * blk + r) * p.o_ld + 8 * qchunk) =
             *reinterpret_cast<const h8*>(buf + r * (2 * C::D) + 16 * qchunk);
     }
@@ -1247,9 +1334,10 @@ template <int D>
 __global__ void __launch_bounds__(256) split_combine_kernel(const float* __restrict__ part_o,
                                                             const float* __restrict__ part_ml, _Float16* o,
                                                             int64_t o_ld, int64_t o_fs, int F, int H, int Lq,
-                                                            int nsplit) {
+                                                            int nsplit, [[maybe_unused]] int64_t o_ext) {
   constexpr int Q = D / 4;
   const int64_t total = (int64_t)F * H * Lq * Q;
+  [[maybe_unused]] const int64_t parts = (int64_t)F * H * nsplit * Lq;  // rows of partials
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
     const int qd = (int)(i % Q);
     int64_t rest = i / Q;
@@ -1258,6 +1346,7 @@ __global__ void __launch_bounds__(256) split_combine_kernel(const float* __restr
     const int hd = (int)(rest % H);
     const int f = (int)(rest / H);
     const int64_t pb = (int64_t)(f * H + hd) * nsplit * Lq + row;  // split s at pb + s * Lq
+    if (!PL_BOUNDS(PL_IN(pb, 1, parts) && PL_IN(pb + (int64_t)(nsplit - 1) * Lq, 1, parts), kSiteCombineIn)) continue;
     float M = -INFINITY;
     for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, part_ml[(pb + (int64_t)sp * Lq) * 2]);
     float L = 0.f;
@@ -1274,7 +1363,8 @@ __global__ void __launch_bounds__(256) split_combine_kernel(const float* __restr
     h4 out;
 #pragma unroll
     for (int k = 0; k < 4; ++k) out[k] = (_Float16)(acc[k] * inv);
-    *reinterpret_cast<h4*>(o + (int64_t)f * o_fs + (int64_t)row * o_ld + (int64_t)hd * D + 4 * qd) = out;
+    if (PL_BOUNDS(PL_IN((int64_t)f * o_fs + (int64_t)row * o_ld + (int64_t)hd * D + 4 * qd, 4, o_ext), kSiteCombineOut))
+      *reinterpret_cast<h4*>(o + (int64_t)f * o_fs + (int64_t)row * o_ld + (int64_t)hd * D + 4 * qd) = out;
   }
 }
 
@@ -1336,6 +1426,9 @@ hipError_t launch_cfg(const KParams& kp, hipStream_t stream, float* workspace) {
     if (p.nsplit > 1) {
       p.part_o = workspace;
       p.part_ml = workspace + (int64_t)p.F * p.H * p.nsplit * p.Lq * D;
+#ifdef PL_DEBUG_BOUNDS
+      p.part_ext = (int64_t)p.F * p.H * p.nsplit * p.Lq * D;
+#endif
     }
   }
   const int64_t blocks = (int64_t)p.nqt * p.F * p.H * p.nsplit;
@@ -1345,8 +1438,13 @@ hipError_t launch_cfg(const KParams& kp, hipStream_t stream, float* workspace) {
   if (hipError_t e = hipGetLastError()) return e;
   const int64_t items = (int64_t)p.F * p.H * p.Lq * (D / 4);
   const int64_t cblocks = std::min<int64_t>((items + 255) / 256, 4096);
+#ifdef PL_DEBUG_BOUNDS
+  const int64_t o_ext = p.o_ext;
+#else
+  const int64_t o_ext = 0;
+#endif
   hipLaunchKernelGGL(split_combine_kernel<D>, dim3((unsigned)cblocks), dim3(256), 0, stream, p.part_o, p.part_ml,
-                     p.o, p.o_ld, p.o_fs, p.F, p.H, p.Lq, p.nsplit);
+                     p.o, p.o_ld, p.o_fs, p.F, p.H, p.Lq, p.nsplit, o_ext);
   return hipGetLastError();
 }
 
@@ -1378,6 +1476,19 @@ size_t refbank_attn_workspace_bytes(int32_t F, int32_t Lq, int32_t H, int32_t d,
   return (size_t)F * H * nsplit * Lq * (d + 2) * sizeof(float);
 }
 
+hipError_t debug_bounds_mask(unsigned long long* mask, bool reset) {
+#ifdef PL_DEBUG_BOUNDS
+  hipError_t e = hipMemcpyFromSymbol(mask, HIP_SYMBOL(g_bounds_mask), sizeof(*mask));
+  if (e != hipSuccess || !reset) return e;
+  const unsigned long long zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_bounds_mask), &zero, sizeof(zero));
+#else
+  (void)reset;
+  *mask = 0;
+  return hipErrorNotSupported;
+#endif
+}
+
 hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream) {
   KParams p;
   p.q = a.q;
@@ -1396,6 +1507,17 @@ hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream) {
   p.nsplit = 1;
   p.tps = 1 << 30;
   p.part_o = p.part_ml = nullptr;
+#ifdef PL_DEBUG_BOUNDS
+  {
+    const int64_t width = (int64_t)a.H * a.d;
+    p.q_ext = (int64_t)(a.F - 1) * a.q_frame_stride + (int64_t)(a.Lq - 1) * a.q_ld + width;
+    p.o_ext = (int64_t)(a.F - 1) * a.o_frame_stride + (int64_t)(a.Lq - 1) * a.o_ld + width;
+    for (int i = 0; i < PL_MAX_SEGMENTS; ++i)
+      p.seg_ext[i] = i < a.nseg ? (int64_t)(a.F - 1) * a.seg[i].frame_stride + (a.seg[i].len - 1) * a.seg[i].ld + width
+                                : 0;
+    p.part_ext = 0;
+  }
+#endif
   float* ws = static_cast<float*>(a.workspace);
   // a single segment of at most one tile: the short-context kernel
   if (a.nseg == 1 && a.seg[0].len <= 64) {

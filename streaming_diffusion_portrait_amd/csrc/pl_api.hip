@@ -374,6 +374,16 @@ pl_status pl_refbank_attn_chunked(const void* q, int64_t q_ld, int64_t q_frame_s
   return ok();
 }
 
+pl_status pl_debug_bounds(uint64_t* mask, int32_t reset) {
+  if (!mask) return fail(PL_EINVAL, "pl_debug_bounds: mask must be non-null");
+  unsigned long long m = 0;
+  const hipError_t e = pl::debug_bounds_mask(&m, reset != 0);
+  *mask = m;
+  if (e == hipErrorNotSupported)
+    return fail(PL_EUNSUPPORTED, "pl_debug_bounds: this library was built without PL_DEBUG_BOUNDS");
+  return device_status(e, "pl_debug_bounds");
+}
+
 pl_status pl_refbank_attn_noalloc(const void* q, int64_t q_ld, int64_t q_frame_stride, void* o, int64_t o_ld,
                                   int64_t o_frame_stride, int32_t F, int32_t Lq, int32_t H, int32_t d,
                                   const pl_kv_segment* segs, int32_t nseg, float scale, void* stream) {

@@ -37,6 +37,10 @@ size_t refbank_attn_workspace_bytes(int32_t F, int32_t Lq, int32_t H, int32_t d,
 // Launch the flash-style MFMA attention for one layer on `stream`.
 hipError_t launch_refbank_attn(const AttnLaunch& a, hipStream_t stream);
 
+// Bounds-checking builds: read (and optionally clear) the mask of access sites
+// that failed their check; hipErrorNotSupported in other builds.
+hipError_t debug_bounds_mask(unsigned long long* mask, bool reset);
+
 // ---- pyramid DDIM -------------------------------------------------------------
 struct DdimLaunch {
   const float* x_t;

@@ -46,8 +46,19 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_debug_bounds_outside_a_checking_build(lib):
+    """The normal build answers the bounds report with PL_EUNSUPPORTED and a
+    zero mask, before any HIP call; a NULL mask is PL_EINVAL."""
+    mask = ctypes.c_uint64(123)
+    assert lib.pl_debug_bounds(ctypes.byref(mask), 1) == B.PL_EUNSUPPORTED
+    assert mask.value == 0
+    assert "PL_DEBUG_BOUNDS" in B.last_error()
+    assert lib.pl_debug_bounds(None, 0) == B.PL_EINVAL
+    assert B.debug_bounds() is None
+
+
 def test_version_and_status_strings(lib):
-    assert lib.pl_abi_version() == 4
+    assert lib.pl_abi_version() == 5
     assert [B.status_name(s) for s in range(4)] == ["PL_OK", "PL_EINVAL", "PL_EUNSUPPORTED", "PL_EDEVICE"]
     assert B.status_name(99) == "PL_UNKNOWN"
 
