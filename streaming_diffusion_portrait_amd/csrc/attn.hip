@@ -68,6 +68,7 @@
 #include "pl_internal.h"
 
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 namespace pl {
@@ -1377,19 +1378,21 @@ int64_t attn_workgroups(int F, int Lq, int H) {
 #ifndef PL_SPLIT_TARGET_WGS
 #define PL_SPLIT_TARGET_WGS 256  // d = 160 workgroups the GPU holds at once (one per CU: LDS)
 #endif
-#ifndef PL_SPLIT_MIN_TILES
-#define PL_SPLIT_MIN_TILES 8  // key tiles a split must keep to win back its partials' write and merge
-#endif
 
 // How many key splits a launch takes (and the tiles per split): only for the
 // head dim whose workgroups take a whole CU each (d = 160, the 16^2 and 8^2
-// levels: a 127.5 KB copy ring, one wave per SIMD), only as far as the launch
-// leaves CUs idle -- more workgroups than CUs would run in a second
-// generation and lose what the split gains -- and only with at least
-// PL_SPLIT_MIN_TILES tiles per split: a workgroup's fixed cost (its first
-// loads, the exact first tile) is several tiles' worth, and the partials'
-// round trip costs about five (measured: the 8^2 level's 5 tiles in two
-// splits took 23.5 us against 20.1 us in one pass).
+// levels: a 127.5 KB copy ring, one wave per SIMD), and only as far as the
+// launch leaves CUs idle -- more workgroups than CUs would run in a second
+// generation and lose what the split gains.  Within that, the count follows a
+// cost model fitted to one-frame and 16-frame launches of both levels: a
+// workgroup spends about 1.3 us per key tile, and each split adds a round
+// trip of F*H*Lq*(d+2)*4 bytes of partials (written, then merged) at about
+// 1.5 TB/s, so n splits of T tiles take about 1.3 T/n + c n us, least at
+// n = sqrt(1.3 T / c).  (Measured, d = 160 with the 4x bank: one frame at
+// 16^2, 20 tiles: 5 splits 24.2 us, 10 splits 26.0, 2 splits 31.5, one pass
+// 46.2; one frame at 8^2, 5 tiles: 5 splits 13.7 us, 2 splits 15.4, one pass
+// 15.7; 16 frames at 8^2: 2 splits 21.5 us against 16.3 in one pass, where the
+// model's optimum is 1.4, so no split.)
 template <class C>
 void split_plan(int F, int Lq, int H, const int64_t* seg_len, int nseg, int& nsplit, int& tps) {
   int ntiles = 0;
@@ -1399,9 +1402,11 @@ void split_plan(int F, int Lq, int H, const int64_t* seg_len, int nseg, int& nsp
   if (C::D != 160 || ntiles < 2) return;
   const int64_t wgs = attn_workgroups<C>(F, Lq, H);
   if (2 * wgs > PL_SPLIT_TARGET_WGS) return;
-  const int want = (int)std::min<int64_t>(ntiles / PL_SPLIT_MIN_TILES, PL_SPLIT_TARGET_WGS / wgs);
+  const double tile_us = 1.3, partial_us = (double)F * H * Lq * (C::D + 2) * 4 / 1.5e6;
+  int64_t want = std::llround(std::sqrt(tile_us * ntiles / partial_us));
+  want = std::min<int64_t>(std::min<int64_t>(want, ntiles), PL_SPLIT_TARGET_WGS / wgs);
   if (want < 2) return;
-  tps = (ntiles + want - 1) / want;
+  tps = (int)((ntiles + want - 1) / want);
   nsplit = (ntiles + tps - 1) / tps;
   if (nsplit < 2) {
     nsplit = 1;

@@ -151,11 +151,15 @@ def test_workspace_size(lib):
     assert _wsize(lib, 16, 256, 8, 160, [256] * 5) == 0
     assert _wsize(lib, 16, 64, 8, 160, [64] * 5) == 0
     # one frame of the 16^2 level with the 4x bank (20 key tiles, 16 workgroups):
-    # two splits of ten tiles; partial O, offset and row sum in fp32 per
-    # (frame, head, split, row)
-    assert _wsize(lib, 1, 256, 8, 160, [256] * 5) == 1 * 8 * 2 * 256 * (160 + 2) * 4
-    # 41 tiles, one workgroup: five splits of at least eight tiles
-    assert _wsize(lib, 1, 40, 1, 160, [64, 1024, 1024, 512]) == 5 * 40 * 162 * 4
+    # five splits of four tiles (the split count minimises 1.3 us per tile per
+    # split against each split's partials round trip); partial O, offset and
+    # row sum in fp32 per (frame, head, split, row)
+    assert _wsize(lib, 1, 256, 8, 160, [256] * 5) == 1 * 8 * 5 * 256 * (160 + 2) * 4
+    # one frame of the 8^2 level: five splits of one tile; two frames of 16^2: four
+    assert _wsize(lib, 1, 64, 8, 160, [64] * 5) == 1 * 8 * 5 * 64 * 162 * 4
+    assert _wsize(lib, 2, 256, 8, 160, [256] * 5) == 2 * 8 * 4 * 256 * 162 * 4
+    # 41 tiles, one workgroup, 40 rows (tiny partials): one tile per split
+    assert _wsize(lib, 1, 40, 1, 160, [64, 1024, 1024, 512]) == 41 * 40 * 162 * 4
     # a single key tile has nothing to split; short contexts take their own kernel
     assert _wsize(lib, 1, 64, 8, 160, [64]) == 0
     assert _wsize(lib, 1, 64, 8, 160, [32]) == 0

@@ -61,13 +61,13 @@ def run(B, q, segs, H, workspace=None):
 
 
 CASES = [
-    # (name, F, L, H, segspec): a split keeps at least 8 key tiles and the
-    # launch must leave CUs idle, so these are few-frame launches with long
-    # key axes; the boundaries fall inside segments and next to ragged tiles
-    ("ragged segments, two splits", 1, 64, 2,
+    # (name, F, L, H, segspec): the launch must leave CUs idle, so these are
+    # few-frame launches with long key axes; the boundaries fall inside
+    # segments and next to ragged tiles
+    ("ragged segments, one tile per split", 1, 64, 2,
      [(100, False, 1.0), (64, True, 1.0), (30, True, 1.0), (129, True, 1.0), (600, True, 1.0), (150, True, 1.0)]),
-    ("one frame, five splits", 1, 40, 1, [(64, False, 1.0), (1024, True, 1.0), (1024, True, 1.0), (512, True, 1.0)]),
-    ("query tail beyond one block", 2, 57, 2, [(57, False, 1.0), (512, True, 1.0), (512, True, 1.0)]),
+    ("one frame, 41 splits", 1, 40, 1, [(64, False, 1.0), (1024, True, 1.0), (1024, True, 1.0), (512, True, 1.0)]),
+    ("query tail beyond one block, two tiles per split", 2, 57, 2, [(57, False, 1.0), (512, True, 1.0), (512, True, 1.0)]),
     ("16 frames x 8 heads, boundary inside a segment", 16, 64, 8,
      [(64, False, 1.0), (256, True, 1.0), (512, True, 1.0), (256, True, 1.0)]),
     ("16 frames x 8 heads, ragged tiles", 16, 64, 8,
@@ -120,8 +120,7 @@ def test_one_frame_levels_split(B):
         say("one-frame split, L =", L)
         lay = inputs.attention_layer(60 + L, 1, L, 1280, 3)
         segs = [(lay["k_self"], lay["v_self"], False)] + [(k, v, True) for k, v in zip(lay["bank_k"], lay["bank_v"])]
-        if L == 256:
-            assert B.workspace_size(1, L, 8, 160, [L] * 5) > 0
+        assert B.workspace_size(1, L, 8, 160, [L] * 5) > 0
         got = run(B, lay["q"], segs, 8)
         assert_attn_close(got, refbank_attention(lay["q"], segs, 8), f"one frame L={L}")
 
