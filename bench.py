@@ -388,6 +388,29 @@ def main():
         del kq, ksegs, ko
     log("  key split (one frame, 4x bank): " +
         ", ".join(f"L={r['L']} split {r['split_us']:.1f} us / single {r['single_pass_us']:.1f} us" for r in key_split))
+    # block-causal attention over chunked sequences (pl_refbank_attn_chunked): the 64^2
+    # level's 4096 tokens per frame as 4 chunks of 1024, each row seeing its own chunk,
+    # the earlier ones (all, or only the previous one) and the reference; FLOPs count
+    # only the keys a row sees
+    chunked = []
+    g = torch.Generator(device=dev).manual_seed(4096 + 17)
+    cq = torch.randn(F, 4096, 320, device=dev, generator=g).half()
+    ck = torch.randn(F, 4096, 320, device=dev, generator=g).half()
+    cv = torch.randn(F, 4096, 320, device=dev, generator=g).half()
+    cbk = torch.randn(4096, 320, device=dev, generator=g).half()
+    cbv = torch.randn(4096, 320, device=dev, generator=g).half()
+    co = torch.empty_like(cq)
+    for hist in (-1, 1):
+        nch, cl = 4, 1024
+        keys = [cl * (c + 1 - (max(0, c - hist) if hist >= 0 else 0)) + 4096 for c in range(nch)]
+        c_flops = sum(4 * F * cl * k * 320 for k in keys)
+        c_us = time_it(lambda: B.chunked_attn(cq, (ck, cv), [(cbk, cbv)], H, cl, hist, out=co), n=20)
+        chunked.append(dict(L=4096, C=320, chunk_len=cl, chunks=nch, max_history=hist, bank=4096, launches=nch,
+                            us=round(c_us, 2), tflops=round(c_flops / (c_us * 1e-6) / 1e12, 1),
+                            pct_fp16_peak=round(100 * c_flops / (c_us * 1e-6) / 1e12 / PEAK_FP16_TFLOPS, 2)))
+    del cq, ck, cv, cbk, cbv, co
+    log("  block-causal chunks (64^2, 4 x 1024 + reference): " +
+        ", ".join(f"history {r['max_history']}: {r['us']:.0f} us {r['tflops']:.0f} TFLOP/s" for r in chunked))
     # the projections either side of the attention: fused q/k/v ([3C, C]) and the
     # output projection ([C, C] + bias) over the 16 frames of each level
     projections = []
@@ -507,6 +530,7 @@ def main():
         "pile_prefill_us": round(prefill_us, 2),
         "expression_cross_attention": short_ctx,
         "key_split_one_frame": key_split,
+        "block_causal_chunks": chunked,
         "projections": projections,
         "motion_us": round(motion_us, 2),
         "layers": layer_report,
